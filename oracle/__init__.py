@@ -1,0 +1,14 @@
+"""Independent CPU oracle for sink-aware GQA attention.
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The product path (``gqa_attention_sink_amd``)
+never imports it, and it imports nothing from the product path.
+"""
+from .sink_attention import (  # noqa: F401
+    sink_attention,
+    sink_attention_decode,
+    sink_attention_chunked,
+    merge_partials,
+    plan_chunks,
+    flops_causal,
+)

@@ -1,0 +1,305 @@
+"""Throughput of sink-aware GQA attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole decode hot path (split-KV kernel + log-sum-exp
+merge) over the gpt-oss-like decode batch (64 sequences, 1 query token, Hq 64 over
+Hkv 8, head_dim 64, KV lengths uniform in [1024, 8192]), with inputs resident in HBM.
+Before every step a 512 MiB write evicts the 256 MB Infinity Cache and the L2s, so
+each step streams its K/V from HBM; only the attention kernels sit inside the timed
+event pair.  The line also reports the other workloads (varlen and long prefill in
+TFLOP/s, speculative decode in GB/s) and the fp64 CPU oracle on a bounded sample.
+
+Algorithmic work (implementation overheads such as split partials are not counted):
+  decode bytes  = K+V of every visible key once per KV head + Q + out + lse + sinks +
+                  kv_indptr;  split kernel bytes = the same minus out and lse.
+  prefill flops = 4 * head_dim * Hq * (visible query-key pairs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FLUSH_BYTES = 512 << 20
+
+
+def _say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _pairs(lens_q, lens_kv, causal):
+    tot = 0
+    for lq, lk in zip(lens_q, lens_kv):
+        if not causal:
+            tot += lq * lk
+            continue
+        i = np.arange(lq, dtype=np.int64)
+        tot += int(np.clip(i + lk - lq + 1, 0, lk).sum())
+    return tot
+
+
+def decode_bytes(w, split_only=False):
+    kv = sum(w.lens_kv) * w.hkv * w.d * 2 * 2
+    q = w.q.numel() * 2
+    small = w.hq * 4 + (w.batch + 1) * 4
+    if split_only:
+        return kv + q + small
+    return kv + q + q + w.batch * w.q_len * w.hq * 4 + small
+
+
+def prefill_flops(w):
+    return 4 * w.d * w.hq * _pairs(w.lens_q, w.lens_kv, w.causal)
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, n):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+    def mark(self, i, j):
+        self.ev[i][j].record(torch.cuda.current_stream())
+
+    def ms(self, j0, j1):
+        return [e[j0].elapsed_time(e[j1]) for e in self.ev]
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_attention_sink_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_for(kernel, workload):
+    """HBM traffic measured by rocprofv3 counters for this kernel and workload, if the
+    committed measurement was taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{kernel}:{workload}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != _source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_decode(sa, w, steps, warmup, flush):
+    ws = torch.empty(sa.decode_workspace_bytes(w.batch, w.q_len, w.hq, w.d, w.max_kv,
+                                               w.num_splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(w.q)
+    lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
+    s = sa.decode_num_slots(w.max_kv, w.num_splits)
+    rows = w.batch * w.q_len * w.hq
+    po = torch.empty((rows, s, w.d), dtype=torch.float32, device="cuda")
+    pl = torch.empty((rows, s), dtype=torch.float32, device="cuda")
+
+    def step_full(t=None, i=0):
+        flush.zero_()
+        if t: t.mark(i, 0)
+        sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal,
+                  w.num_splits, workspace=ws, out=out, lse=lse)
+        if t: t.mark(i, 1)
+
+    def step_split(t, i):
+        flush.zero_()
+        t.mark(i, 0)
+        sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                          w.causal, w.num_splits, part_o=po, part_lse=pl)
+        t.mark(i, 1)
+        sa.merge(po, pl, out=out.view(rows, w.d), lse=lse.view(rows))
+        t.mark(i, 2)
+
+    for _ in range(warmup):
+        step_full()
+    torch.cuda.synchronize()
+    t = Timer(steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_full(t, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    full_ms = t.ms(0, 1)
+    # the split kernel on its own (same launches as inside decode)
+    t2 = Timer(steps)
+    for i in range(steps):
+        step_split(t2, i)
+    torch.cuda.synchronize()
+    split_ms = t2.ms(0, 1)
+    merge_ms = t2.ms(1, 2)
+    return dict(full_ms=float(np.mean(full_ms)), full_ms_min=float(np.min(full_ms)),
+                split_ms=float(np.mean(split_ms)), merge_ms=float(np.mean(merge_ms)),
+                wall_s=wall, slots=s)
+
+
+def bench_prefill(sa, w, steps, warmup, flush):
+    out = torch.empty_like(w.q)
+    lse = torch.empty((w.q.shape[0], w.hq), dtype=torch.float32, device="cuda")
+
+    def step(t=None, i=0):
+        flush.zero_()
+        if t: t.mark(i, 0)
+        sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q, w.scale,
+                   w.causal, out=out, lse=lse)
+        if t: t.mark(i, 1)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(t, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = t.ms(0, 1)
+    return dict(ms=float(np.mean(ms)), ms_min=float(np.min(ms)), wall_s=wall)
+
+
+def cpu_baseline(w_gpu, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of the decode workload: whole sequences,
+    taken in order until about budget_s seconds of CPU work; the rate is scaled to the
+    metric's unit (algorithmic GB/s of the sample)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    ind = w_gpu.cu_seqlens_kv.cpu().tolist()
+    done_bytes, t_used, nseq = 0, 0.0, 0
+    for b in range(w_gpu.batch):
+        ks = slice(ind[b], ind[b + 1])
+        q = w_gpu.q[b:b + 1].cpu()
+        k = w_gpu.k[:, ks].cpu()
+        v = w_gpu.v[:, ks].cpu()
+        t0 = time.perf_counter()
+        oracle.sink_attention_decode(q, k, v, w_gpu.sinks, [0, ind[b + 1] - ind[b]],
+                                     w_gpu.scale, w_gpu.causal)
+        t_used += time.perf_counter() - t0
+        lk = ind[b + 1] - ind[b]
+        done_bytes += lk * w_gpu.hkv * w_gpu.d * 4 + 2 * q.numel() * 2 + w_gpu.q_len * w_gpu.hq * 4
+        nseq += 1
+        if t_used >= budget_s:
+            break
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{nseq} of {w_gpu.batch} sequences of {w_gpu.name} (all heads), "
+                      f"{t_used:.1f} s of fp64 numpy on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_gptoss")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(decode shards by sequence and prefill by head with no exchange inside "
+              "attention); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import gqa_attention_sink_amd as sa
+    from gqa_attention_sink_amd import workloads as wl
+    if not os.path.exists(sa.LIB_PATH):
+        from gqa_attention_sink_amd.build import build
+        build()
+    sa.load()
+    torch.cuda.set_device(0)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    _say(f"workload {args.workload}")
+    w = wl.make(args.workload, device="cuda")
+    assert w.kind == "decode", "the headline step is the decode path"
+    r = bench_decode(sa, w, args.steps, args.warmup, flush)
+    nbytes = decode_bytes(w)
+    split_bytes = decode_bytes(w, split_only=True)
+    value = nbytes / (r["full_ms"] * 1e-3) / 1e9
+    split_gbs = split_bytes / (r["split_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "sink-attn decode HBM GB/s (and prefill TFLOP/s) on 1 MI355X, % of peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["full_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "hq": w.hq,
+                   "hkv": w.hkv, "head_dim": w.d, "sum_kv": sum(w.lens_kv),
+                   "num_splits": w.num_splits, "slots": r["slots"], "seed": w.seed,
+                   "parallelism": "single-gpu"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_min": round(r["full_ms_min"], 4),
+        "wall_ms_per_step_incl_flush": round(r["wall_s"] * 1e3 / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
+                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic_for("decode_split_kernel", w.name),
+                     "algorithmic_bytes_per_launch": split_bytes,
+                     "avg_launch_ms": round(r["split_ms"], 4),
+                     "merge_ms": round(r["merge_ms"], 4)},
+    }
+    others = {}
+    if not args.no_others:
+        del w
+        torch.cuda.empty_cache()
+        for name in ("varlen_prefill", "long_prefill"):
+            _say(f"workload {name}")
+            p = wl.make(name, device="cuda")
+            rp = bench_prefill(sa, p, args.steps, args.warmup, flush)
+            fl = prefill_flops(p)
+            tf = fl / (rp["ms"] * 1e-3) / 1e12
+            others[name] = {"TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                            "ms": round(rp["ms"], 4), "ms_min": round(rp["ms_min"], 4),
+                            "flops": fl}
+            del p
+            torch.cuda.empty_cache()
+        _say("workload spec_decode")
+        d5 = wl.make("spec_decode", device="cuda")
+        r5 = bench_decode(sa, d5, max(5, args.steps // 2), 2, flush)
+        b5 = decode_bytes(d5)
+        g5 = b5 / (r5["full_ms"] * 1e-3) / 1e9
+        s5 = decode_bytes(d5, True) / (r5["split_ms"] * 1e-3) / 1e9
+        others["spec_decode"] = {"GB/s": round(g5, 2), "frac_of_hbm_peak": round(g5 / HBM_PEAK_GBS, 4),
+                                 "ms": round(r5["full_ms"], 4), "split_kernel_GB/s": round(s5, 2),
+                                 "split_ms": round(r5["split_ms"], 4),
+                                 "merge_ms": round(r5["merge_ms"], 4), "bytes": b5}
+        del d5
+        torch.cuda.empty_cache()
+        line["others"] = others
+    if not args.no_cpu_baseline:
+        _say("cpu baseline (oracle)")
+        w = wl.make(args.workload, device="cuda")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

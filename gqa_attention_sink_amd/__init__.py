@@ -1,0 +1,17 @@
+"""gqa_attention_sink_amd: grouped-query attention with a learned per-head softmax sink,
+as hand-written HIP kernels for MI355X (gfx950) behind a C ABI (include/sink_attn.h).
+
+    from gqa_attention_sink_amd import prefill, decode
+"""
+from .sink_attn import (  # noqa: F401
+    LIB_PATH,
+    SinkAttnError,
+    decode,
+    decode_num_slots,
+    decode_partial,
+    decode_workspace_bytes,
+    load,
+    merge,
+    prefill,
+    version,
+)

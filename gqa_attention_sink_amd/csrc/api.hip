@@ -1,0 +1,250 @@
+// C ABI of libsinkattn: argument validation, planning and launch.  Every
+// host-checkable precondition is checked before the first HIP call; no C++ exception
+// crosses the boundary.
+#include <math.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "../../include/sink_attn.h"
+#include "sa_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxSplits = 64;
+constexpr int kMaxSlots = 256;
+constexpr int64_t kMaxSpanBytes = 0x7fffffffLL;  // bounded-load window of one sequence
+
+inline int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return SINK_ATTN_ERR_HIP;
+}
+
+inline bool dim_ok(int d) { return d == 64 || d == 128; }
+
+inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+inline int planned_slots(int32_t max_kv_len, int32_t num_splits) {
+  if (num_splits > 0) return num_splits;
+  int n = (int)((max_kv_len + 511) / 512);
+  return n < 4 ? 4 : (n > 16 ? 16 : n);
+}
+
+// Query heads per prefill workgroup: the largest divisor of the GQA group size <= 4.
+inline int heads_per_wg(int group) {
+  for (int hg = 4; hg >= 1; --hg)
+    if (group % hg == 0) return hg;
+  return 1;
+}
+
+int check_decode_args(const void* q, const void* k, const void* v, const int32_t* kv_indptr,
+                      int32_t batch, int32_t q_len, int64_t total_kv, int32_t max_kv_len,
+                      int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t causal,
+                      int32_t num_splits) {
+  if (!q || !k || !v || !kv_indptr) return SINK_ATTN_ERR_INVALID_ARG;
+  if (batch < 1 || hq < 1 || hkv < 1 || total_kv < 0 || max_kv_len < 0)
+    return SINK_ATTN_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return SINK_ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(sm_scale)) return SINK_ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SINK_ATTN_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > kMaxSplits) return SINK_ATTN_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > 4) return SINK_ATTN_ERR_UNSUPPORTED;
+  if (!dim_ok(d)) return SINK_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)max_kv_len * d * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)q_len * hq * d * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)batch * q_len * hq > ((int64_t)1 << 40)) return SINK_ATTN_ERR_UNSUPPORTED;
+  return SINK_ATTN_OK;
+}
+
+sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const float* sinks,
+                           const int32_t* kv_indptr, int32_t q_len, int64_t total_kv,
+                           int32_t max_kv_len, int32_t hq, int32_t hkv, float sm_scale,
+                           int32_t causal, int32_t num_splits) {
+  sa::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sinks = sinks;
+  a.kv_indptr = kv_indptr;
+  a.total_kv = total_kv;
+  a.q_len = q_len;
+  a.num_q_heads = hq;
+  a.group = hq / hkv;
+  a.row_groups = (q_len * a.group + 63) / 64;
+  a.num_splits = num_splits;
+  a.num_slots = planned_slots(max_kv_len, num_splits);
+  a.causal = causal;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sink_attn_status_str(int status) {
+  switch (status) {
+    case SINK_ATTN_OK: return "SINK_ATTN_OK";
+    case SINK_ATTN_ERR_INVALID_ARG: return "SINK_ATTN_ERR_INVALID_ARG: invalid argument";
+    case SINK_ATTN_ERR_UNSUPPORTED: return "SINK_ATTN_ERR_UNSUPPORTED: unsupported size or head_dim";
+    case SINK_ATTN_ERR_WORKSPACE: return "SINK_ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case SINK_ATTN_ERR_HIP: return "SINK_ATTN_ERR_HIP: a HIP call failed";
+    case SINK_ATTN_ERR_INTERNAL: return "SINK_ATTN_ERR_INTERNAL: internal error";
+    default: return "unknown sink_attn status";
+  }
+}
+
+int sink_attn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* sink_attn_version(void) { return "0.1.0"; }
+
+int sink_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                      int32_t max_seqlen_q, int64_t total_q, int64_t total_kv,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      float sm_scale, int32_t causal, void* out, float* lse, void* stream) {
+  try {
+    if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_kv || !out) return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seqlen_q < 0 || total_q < 0 ||
+        total_kv < 0)
+      return SINK_ATTN_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return SINK_ATTN_ERR_INVALID_ARG;
+    if (!scale_ok(sm_scale)) return SINK_ATTN_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return SINK_ATTN_ERR_INVALID_ARG;
+    if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)64 * num_q_heads * head_dim * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (max_seqlen_q == 0 || total_q == 0) return SINK_ATTN_OK;  // nothing to compute
+
+    sa::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.sinks = sinks;
+    a.cu_q = cu_seqlens_q;
+    a.cu_kv = cu_seqlens_kv;
+    a.total_kv = total_kv;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.hg = heads_per_wg(a.group);
+    a.pw = 4 / a.hg;
+    a.n_hgroups = a.group / a.hg;
+    a.n_qtiles = (max_seqlen_q + 64 * a.pw - 1) / (64 * a.pw);
+    a.causal = causal;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    if (a.n_qtiles > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int32_t sink_attn_decode_num_slots(int32_t max_kv_len, int32_t num_splits) {
+  if (max_kv_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return 0;
+  return planned_slots(max_kv_len, num_splits);
+}
+
+size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                        int32_t head_dim, int32_t max_kv_len,
+                                        int32_t num_splits) {
+  if (batch < 1 || q_len < 1 || q_len > 4 || num_q_heads < 1 || !dim_ok(head_dim) ||
+      max_kv_len < 0 || num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  const int64_t S = planned_slots(max_kv_len, num_splits);
+  int64_t bytes = rows * S * head_dim * 4;   // partial outputs
+  bytes = (bytes + 255) & ~(int64_t)255;
+  bytes += rows * S * 4;                     // partial lse
+  return (size_t)((bytes + 255) & ~(int64_t)255);
+}
+
+int sink_attn_decode_partial(const void* q, const void* k, const void* v, const float* sinks,
+                             const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                             int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                             int32_t causal, int32_t num_splits, float* part_o,
+                             float* part_lse, void* stream) {
+  try {
+    int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len,
+                               num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
+    if (rc != SINK_ATTN_OK) return rc;
+    if (!part_o || !part_lse) return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+                                   num_q_heads, num_kv_heads, sm_scale, causal, num_splits);
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_decode(const void* q, const void* k, const void* v, const float* sinks,
+                     const int32_t* kv_indptr, int32_t batch, int32_t q_len, int64_t total_kv,
+                     int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float sm_scale, int32_t causal, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* out, float* lse,
+                     void* stream) {
+  try {
+    int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len,
+                               num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
+    if (rc != SINK_ATTN_OK) return rc;
+    if (!out) return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+                                   num_q_heads, num_kv_heads, sm_scale, causal, num_splits);
+    hipStream_t st = (hipStream_t)stream;
+    if (a.num_slots == 1) {  // one chunk per sequence: the split kernel writes the result
+      a.out = out;
+      a.lse = lse;
+      hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, st);
+      if (e != hipSuccess) return hip_fail(e);
+      return SINK_ATTN_OK;
+    }
+    const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, head_dim,
+                                                         max_kv_len, num_splits);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+      return SINK_ATTN_ERR_WORKSPACE;
+    const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+    int64_t obytes = rows * a.num_slots * head_dim * 4;
+    obytes = (obytes + 255) & ~(int64_t)255;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + obytes);
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_merge(const float* part_o, const float* part_lse, int64_t rows, int32_t num_slots,
+                    int32_t head_dim, void* out, float* lse, void* stream) {
+  try {
+    if (!part_o || !part_lse || !out || rows < 0) return SINK_ATTN_ERR_INVALID_ARG;
+    if (num_slots < 1 || num_slots > kMaxSlots) return SINK_ATTN_ERR_INVALID_ARG;
+    if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
+    if ((rows + 3) / 4 > 0x7fffffffLL) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (rows == 0) return SINK_ATTN_OK;
+    hipError_t e = sa::launch_merge(part_o, part_lse, rows, num_slots, head_dim, out, lse,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device helpers for the gfx950 sink-attention kernels: MFMA wrappers, bounded
+// buffer loads, bf16 packing and the exp2-domain online-softmax constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Raw buffer descriptor word 3 for gfx9-family raw (untyped) buffers.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A bounded view of `bytes` bytes at `base`: loads at offsets >= bytes return zero
+// instead of touching memory, which is how every tail (keys past a sequence's end,
+// queries past a tile) is handled without branches or faults.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16, fp32) += A(16x32) * B(32x16), bf16 inputs.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// D(32x32, fp32) += A(32x16) * B(16x32), bf16 inputs.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 with round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// Halves of two packed bf16 pairs: (lo16(x), lo16(y)) and (hi16(x), hi16(y)).
+__device__ __forceinline__ uint32_t lo_lo(uint32_t x, uint32_t y) {
+  return (x & 0xffffu) | (y << 16);
+}
+__device__ __forceinline__ uint32_t hi_hi(uint32_t x, uint32_t y) {
+  return (x >> 16) | (y & 0xffff0000u);
+}
+
+}  // namespace sa

@@ -1,0 +1,251 @@
+"""ctypes binding of libsinkattn.so: argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the library
+is missing or no GPU is present the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
+
+_lib = None
+
+_SIGS = {
+    "sink_attn_prefill": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_decode": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
+    "sink_attn_decode_partial": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_decode_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32]),
+    "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
+    "sink_attn_merge": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "sink_attn_last_hip_error": (ctypes.c_int, []),
+    "sink_attn_version": (ctypes.c_char_p, []),
+}
+
+
+def load() -> ctypes.CDLL:
+    """Load (once) the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m gqa_attention_sink_amd.build`"
+                " (there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class SinkAttnError(RuntimeError):
+    pass
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        msg = lib.sink_attn_status_str(rc).decode()
+        if rc == 4:
+            msg += f" (hipError {lib.sink_attn_last_hip_error()})"
+        raise SinkAttnError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _dev_tensor(t: torch.Tensor, dtype, name: str, ndim: Optional[int] = None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if ndim is not None:
+        _need(t.dim() == ndim, f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _sinks_arg(sinks, hq, device):
+    if sinks is None:
+        return None
+    _dev_tensor(sinks, torch.float32, "sinks", 1)
+    _need(sinks.numel() == hq and sinks.device == device, "sinks must be [Hq] on q's device")
+    return sinks
+
+
+def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
+            sm_scale: Optional[float] = None, causal: bool = True, out=None, lse=None,
+            return_lse: bool = True):
+    """Variable-length sink attention prefill.
+
+    q [total_q, Hq, D] bf16; k, v [Hkv, total_kv, D] bf16 (HND); sinks fp32 [Hq] or
+    None; cu_seqlens_q / cu_seqlens_kv int32 [B+1] on the GPU; max_seqlen_q a host int.
+    Returns (out [total_q, Hq, D] bf16, lse [total_q, Hq] fp32 or None)."""
+    lib = load()
+    _dev_tensor(q, torch.bfloat16, "q", 3)
+    _dev_tensor(k, torch.bfloat16, "k", 3)
+    _dev_tensor(v, torch.bfloat16, "v", 3)
+    _dev_tensor(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _dev_tensor(cu_seqlens_kv, torch.int32, "cu_seqlens_kv", 1)
+    tq, hq, d = q.shape
+    hkv, tk, dk = k.shape
+    _need(v.shape == k.shape and dk == d, "k and v must be [Hkv, total_kv, D] matching q")
+    _need(cu_seqlens_q.numel() == cu_seqlens_kv.numel() and cu_seqlens_q.numel() >= 2,
+          "cu_seqlens must both be [B+1]")
+    batch = cu_seqlens_q.numel() - 1
+    sinks = _sinks_arg(sinks, hq, q.device)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, torch.bfloat16, "out", 3)
+        _need(out.shape == q.shape, "out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev_tensor(lse, torch.float32, "lse", 2)
+        _need(tuple(lse.shape) == (tq, hq), "lse must be [total_q, Hq]")
+    rc = lib.sink_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), tq, tk, hq, hkv,
+                               d, scale, int(bool(causal)), _ptr(out), _ptr(lse),
+                               _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def decode_num_slots(max_kv_len: int, num_splits: int = 0) -> int:
+    return int(load().sink_attn_decode_num_slots(int(max_kv_len), int(num_splits)))
+
+
+def decode_workspace_bytes(batch: int, q_len: int, num_q_heads: int, head_dim: int,
+                           max_kv_len: int, num_splits: int = 0) -> int:
+    return int(load().sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, head_dim,
+                                                       int(max_kv_len), int(num_splits)))
+
+
+def _decode_common(q, k, v, kv_indptr):
+    _dev_tensor(q, torch.bfloat16, "q", 4)
+    _dev_tensor(k, torch.bfloat16, "k", 3)
+    _dev_tensor(v, torch.bfloat16, "v", 3)
+    _dev_tensor(kv_indptr, torch.int32, "kv_indptr", 1)
+    b, ql, hq, d = q.shape
+    hkv, tk, dk = k.shape
+    _need(v.shape == k.shape and dk == d, "k and v must be [Hkv, total_kv, D] matching q")
+    _need(kv_indptr.numel() == b + 1, "kv_indptr must be [batch+1]")
+    return b, ql, hq, d, hkv, tk
+
+
+def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
+           causal: bool = True, num_splits: int = 0, workspace=None, out=None, lse=None,
+           return_lse: bool = True):
+    """Split-KV decode with log-sum-exp merge.
+
+    q [B, q_len, Hq, D] bf16 (q_len 1..4); k, v [Hkv, total_kv, D] bf16 (HND);
+    kv_indptr int32 [B+1] (the KV already holds the q_len new tokens); max_kv_len a
+    host int.  workspace: a uint8 GPU tensor of at least decode_workspace_bytes(...)
+    bytes (allocated here if None).  Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq])."""
+    lib = load()
+    b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
+    sinks = _sinks_arg(sinks, hq, q.device)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    nbytes = decode_workspace_bytes(b, ql, hq, d, max_kv_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _dev_tensor(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, torch.bfloat16, "out", 4)
+        _need(out.shape == q.shape, "out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((b, ql, hq), dtype=torch.float32, device=q.device)
+    rc = lib.sink_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(kv_indptr), b, ql,
+                              tk, int(max_kv_len), hq, hkv, d, scale, int(bool(causal)),
+                              int(num_splits), _ptr(workspace), workspace.numel(), _ptr(out),
+                              _ptr(lse), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
+                   causal: bool = True, num_splits: int = 0, part_o=None, part_lse=None):
+    """First stage of decode alone.  Returns (part_o [B*q_len*Hq, S, D] fp32,
+    part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(max_kv_len, num_splits)."""
+    lib = load()
+    b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
+    sinks = _sinks_arg(sinks, hq, q.device)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    s = decode_num_slots(max_kv_len, num_splits)
+    rows = b * ql * hq
+    if part_o is None:
+        part_o = torch.empty((rows, s, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((rows, s), dtype=torch.float32, device=q.device)
+    _dev_tensor(part_o, torch.float32, "part_o", 3)
+    _dev_tensor(part_lse, torch.float32, "part_lse", 2)
+    _need(tuple(part_o.shape) == (rows, s, d) and tuple(part_lse.shape) == (rows, s),
+          "partial buffers have the wrong shape")
+    rc = lib.sink_attn_decode_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(kv_indptr),
+                                      b, ql, tk, int(max_kv_len), hq, hkv, d, scale,
+                                      int(bool(causal)), int(num_splits), _ptr(part_o),
+                                      _ptr(part_lse), _stream(q.device))
+    _check(rc)
+    return part_o, part_lse
+
+
+def merge(part_o, part_lse, out=None, lse=None, return_lse: bool = True):
+    """Log-sum-exp merge of partials: part_o [rows, S, D] fp32, part_lse [rows, S] fp32
+    -> (out [rows, D] bf16, lse [rows] fp32)."""
+    lib = load()
+    _dev_tensor(part_o, torch.float32, "part_o", 3)
+    _dev_tensor(part_lse, torch.float32, "part_lse", 2)
+    rows, s, d = part_o.shape
+    _need(tuple(part_lse.shape) == (rows, s), "part_lse must be [rows, S]")
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=part_o.device)
+    if lse is None and return_lse:
+        lse = torch.empty((rows,), dtype=torch.float32, device=part_o.device)
+    rc = lib.sink_attn_merge(_ptr(part_o), _ptr(part_lse), rows, s, d, _ptr(out), _ptr(lse),
+                             _stream(part_o.device))
+    _check(rc)
+    return out, lse
+
+
+def version() -> str:
+    return load().sink_attn_version().decode()

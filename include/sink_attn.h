@@ -1,0 +1,158 @@
+/*
+ * sink_attn.h -- C ABI of the gfx950 (MI355X) sink-aware grouped-query attention
+ * library (libsinkattn.so).
+ *
+ * The operation ("GPT-OSS on day 0", section "Kernels for GPT-OSS" > "Sink attention"):
+ * for every query row and query head h,
+ *
+ *     out = softmax( [ q.K^T * sm_scale , sinks[h] ] ) . [ V ; 0 ]
+ *
+ * i.e. the head's sink is one extra logit in the softmax denominator that has no value
+ * row.  The softmax is evaluated online with the running maximum subtracted; the
+ * running state starts at (max = sink, sum = 1); when the key axis is split into
+ * chunks the sink joins the first chunk only and the chunks are combined by a
+ * log-sum-exp merge.  Attention is grouped-query: query head h reads KV head
+ * h / (num_q_heads / num_kv_heads) (same page, "model deltas").  K and V are stored
+ * head-major ("HND": [kv_head][token][head_dim], tokens contiguous per head), the KV
+ * cache layout of "Hosting Qwen on Blackwell" (introduction).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer; the caller owns all memory.  The
+ *    library never allocates, frees or synchronises: work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the legacy default stream) and the call returns at once.
+ *  - bf16 is IEEE bfloat16 (1-8-7); outputs are rounded to nearest even.
+ *  - Causal alignment is bottom-right: query i of a sequence with Lq queries and Lk
+ *    keys sees key j iff j <= i + Lk - Lq.
+ *  - lse is the natural-log partition function of the row INCLUDING the sink term
+ *    (ln(e^sink + sum_j e^(s_j))); -inf for a row with no key and no sink.
+ *  - A NULL `sinks` means no sink (every sink = -inf).  A sink may be -inf per head.
+ *  - Return value: a sink_attn_status.  Every precondition that the host can check is
+ *    checked before any HIP call; device-side preconditions (monotone index arrays,
+ *    offsets within the totals) are documented, not checked, because checking them
+ *    would need a synchronisation -- but every device read of K, V and Q goes through
+ *    bounded buffer loads, so a violation yields wrong numbers, never a fault.
+ *  - Thread-safe; no global mutable state beyond a per-thread last-HIP-error slot.
+ */
+#ifndef SINK_ATTN_H
+#define SINK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SINK_ATTN_OK = 0,
+  SINK_ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, non-finite scale, ...   */
+  SINK_ATTN_ERR_UNSUPPORTED = 2,   /* valid but not instantiated (head_dim, q_len...) */
+  SINK_ATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small                  */
+  SINK_ATTN_ERR_HIP = 4,           /* a HIP call failed; see sink_attn_last_hip_error */
+  SINK_ATTN_ERR_INTERNAL = 5       /* unexpected internal failure                     */
+} sink_attn_status;
+
+/*
+ * Variable-length prefill ("Sink attention": the same sink rule serves prefill).
+ *
+ *  q             bf16 [total_q, num_q_heads, head_dim], token-major, contiguous.
+ *  k, v          bf16 [num_kv_heads, total_kv, head_dim], head-major, contiguous.
+ *  sinks         fp32 [num_q_heads] or NULL.
+ *  cu_seqlens_q  int32 [batch+1], cu_seqlens_q[0] = 0, nondecreasing, last = total_q.
+ *  cu_seqlens_kv int32 [batch+1], likewise over the token axis of k and v.
+ *  max_seqlen_q  host upper bound of cu_seqlens_q[b+1]-cu_seqlens_q[b] (sizes the grid;
+ *                rows beyond it are not computed).
+ *  head_dim      64 or 128.  num_q_heads % num_kv_heads == 0.
+ *  sm_scale      finite, > 0; multiplies q.k (not the sink).
+ *  causal        0 or 1.  When 1, each sequence must have Lk >= Lq (documented).
+ *  out           bf16 [total_q, num_q_heads, head_dim].
+ *  lse           fp32 [total_q, num_q_heads] or NULL.
+ */
+int sink_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                      int32_t batch, int32_t max_seqlen_q, int64_t total_q,
+                      int64_t total_kv, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float sm_scale, int32_t causal, void* out,
+                      float* lse, void* stream);
+
+/*
+ * Decode with 1..4 query tokens per sequence (multi-token / speculative decode), split
+ * along the key axis ("Sink attention": attention parallelised over heads and KV
+ * length; the sink enters the first block only) and merged by log-sum-exp.
+ *
+ *  q          bf16 [batch, q_len, num_q_heads, head_dim].
+ *  k, v       bf16 [num_kv_heads, total_kv, head_dim] (HND).
+ *  kv_indptr  int32 [batch+1]: sequence b owns tokens [kv_indptr[b], kv_indptr[b+1]) of
+ *             the token axis.  The KV already contains the q_len new tokens, so query t
+ *             sits at position Lk - q_len + t; with causal=1 it sees keys <= that
+ *             position (causal within the draft).
+ *  max_kv_len host upper bound of kv_indptr[b+1]-kv_indptr[b].
+ *  num_splits 0 = planner: clamp(ceil(Lk/512), 4, 16) chunks for each sequence;
+ *             k in 1..64 = exactly k chunks per sequence.  A chunk holds
+ *             ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
+ *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,
+ *             256-byte aligned; contents need no initialisation.  Calls that share one
+ *             workspace must be stream-ordered.
+ *  out        bf16 [batch, q_len, num_q_heads, head_dim];  lse fp32 [batch, q_len,
+ *             num_q_heads] or NULL.
+ */
+int sink_attn_decode(const void* q, const void* k, const void* v, const float* sinks,
+                     const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                     int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                     int32_t causal, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
+ * invalid).  Holds fp32 partial outputs and partial lse for every (row, chunk). */
+size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                        int32_t head_dim, int32_t max_kv_len,
+                                        int32_t num_splits);
+
+/* Number of chunk slots per row the decode path uses (the S of the partial layout). */
+int32_t sink_attn_decode_num_slots(int32_t max_kv_len, int32_t num_splits);
+
+/*
+ * First stage of sink_attn_decode on its own: the split kernel writes, for every row
+ * r = (b*q_len + t)*num_q_heads + h and chunk slot c < S, the chunk's normalised
+ * output part_o[r][c][0..head_dim) (fp32) and its natural-log partition function
+ * part_lse[r][c] (fp32; -inf for an empty chunk or an unused slot; chunk 0 includes
+ * the sink).  S = sink_attn_decode_num_slots(max_kv_len, num_splits).  Exported so the
+ * per-chunk partials can be checked and timed; sink_attn_decode = this + merge.
+ */
+int sink_attn_decode_partial(const void* q, const void* k, const void* v,
+                             const float* sinks, const int32_t* kv_indptr, int32_t batch,
+                             int32_t q_len, int64_t total_kv, int32_t max_kv_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             float sm_scale, int32_t causal, int32_t num_splits,
+                             float* part_o, float* part_lse, void* stream);
+
+/*
+ * Log-sum-exp merge of chunk partials ("Sink attention": blocks along the key axis are
+ * combined; the sink is already inside chunk 0's partial).  For each row:
+ *   m* = max_c part_lse[r][c],  w_c = e^(part_lse[r][c] - m*),
+ *   out[r] = sum_c w_c part_o[r][c] / sum_c w_c   (bf16),  lse[r] = m* + ln sum_c w_c.
+ * Slots with part_lse = -inf carry no weight (their part_o is not read); a row with
+ * every slot -inf gets out = 0 and lse = -inf.
+ *  part_o fp32 [rows, num_slots, head_dim], part_lse fp32 [rows, num_slots],
+ *  num_slots 1..256, head_dim 64 or 128, out bf16 [rows, head_dim], lse fp32 [rows] or
+ *  NULL.
+ */
+int sink_attn_merge(const float* part_o, const float* part_lse, int64_t rows,
+                    int32_t num_slots, int32_t head_dim, void* out, float* lse,
+                    void* stream);
+
+/* Static text for a status code. */
+const char* sink_attn_status_str(int status);
+
+/* The hipError_t of the last SINK_ATTN_ERR_HIP returned on the calling thread. */
+int sink_attn_last_hip_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* sink_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H */

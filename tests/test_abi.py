@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point that
+include/sink_attn.h declares, and rejects every invalid argument the host can see
+before making any HIP call."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from gqa_attention_sink_amd import sink_attn as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sink_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.LIB_PATH):
+        from gqa_attention_sink_amd.build import build
+        build()
+    return sa.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?(sink_attn_[a-z_0-9]+)\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_workspace_bytes",
+              "sink_attn_merge", "sink_attn_status_str", "sink_attn_decode_partial"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(ln.split()[-1] for ln in out.splitlines() if ln.strip())
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        assert hasattr(lib, n)
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cq=FAKE, ck=FAKE, batch=1, maxq=16, tq=16,
+             tk=16, hq=8, hkv=2, d=64, scale=0.125, causal=1, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.sink_attn_prefill(a["q"], a["k"], a["v"], a["sinks"], a["cq"], a["ck"],
+                                 a["batch"], a["maxq"], a["tq"], a["tk"], a["hq"], a["hkv"],
+                                 a["d"], a["scale"], a["causal"], a["out"], a["lse"], None)
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, ind=FAKE, batch=2, ql=1, tk=64, maxk=32,
+             hq=8, hkv=2, d=64, scale=0.125, causal=1, ns=0, ws=None, wsb=0, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.sink_attn_decode(a["q"], a["k"], a["v"], a["sinks"], a["ind"], a["batch"],
+                                a["ql"], a["tk"], a["maxk"], a["hq"], a["hkv"], a["d"],
+                                a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["out"],
+                                a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(cq=None), INVALID), (dict(ck=None), INVALID), (dict(out=None), INVALID),
+    (dict(batch=0), INVALID), (dict(hq=6, hkv=4), INVALID), (dict(hkv=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(causal=2), INVALID), (dict(maxq=-1), INVALID), (dict(tq=-5), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), UNSUPPORTED),
+    (dict(maxq=0), OK), (dict(tq=0), OK),
+])
+def test_prefill_validation(lib, kw, rc):
+    assert _prefill(lib, **kw) == rc
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q=None), INVALID), (dict(ind=None), INVALID), (dict(out=None), INVALID),
+    (dict(hq=8, hkv=3), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(ns=-1), INVALID), (dict(ns=65), INVALID), (dict(batch=0), INVALID),
+    (dict(causal=-1), INVALID), (dict(maxk=-3), INVALID),
+    (dict(ql=0), UNSUPPORTED), (dict(ql=5), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+    (dict(maxk=1 << 24, d=128), UNSUPPORTED),
+    (dict(ws=None, wsb=0), WORKSPACE), (dict(ws=FAKE, wsb=16), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1010), wsb=1 << 30), WORKSPACE),  # misaligned
+])
+def test_decode_validation(lib, kw, rc):
+    assert _decode(lib, **kw) == rc
+
+
+def test_decode_partial_validation(lib):
+    f = lib.sink_attn_decode_partial
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 1, 64, 32, 8, 2, 64, 0.125, 1, 0, None, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 9, 64, 32, 8, 2, 64, 0.125, 1, 0, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_merge_validation(lib):
+    m = lib.sink_attn_merge
+    assert m(None, FAKE, 4, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 4, 0, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 4, 257, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, -1, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 4, 2, 72, FAKE, None, None) == UNSUPPORTED
+    assert m(FAKE, FAKE, 0, 2, 64, FAKE, None, None) == OK
+
+
+def test_planner_slots(lib):
+    ns = lib.sink_attn_decode_num_slots
+    assert ns(8192, 0) == 16 and ns(1024, 0) == 4 and ns(100, 0) == 4 and ns(0, 0) == 4
+    assert ns(4097, 0) == 9 and ns(100000, 0) == 16
+    assert ns(32768, 32) == 32 and ns(10, 1) == 1
+    assert ns(10, 65) == 0 and ns(-1, 0) == 0
+
+
+def test_workspace_bytes(lib):
+    wb = lib.sink_attn_decode_workspace_bytes
+    rows, s, d = 256 * 4 * 64, 32, 128
+    o = rows * s * d * 4
+    o = (o + 255) // 256 * 256
+    expect = (o + rows * s * 4 + 255) // 256 * 256
+    assert wb(256, 4, 64, 128, 32768, 32) == expect
+    assert wb(64, 1, 64, 64, 8192, 0) >= 64 * 64 * 16 * 65 * 4
+    assert wb(0, 1, 8, 64, 10, 0) == 0 and wb(1, 5, 8, 64, 10, 0) == 0 and wb(1, 1, 8, 96, 10, 0) == 0
+
+
+def test_status_strings(lib):
+    for rc in range(6):
+        assert lib.sink_attn_status_str(rc).decode().startswith("SINK_ATTN_")
+    assert b"unknown" in lib.sink_attn_status_str(99)
+    assert re.match(rb"\d+\.\d+\.\d+", lib.sink_attn_version())
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sa.prefill(q, k, k, None, cu, cu, 4)

@@ -1,0 +1,365 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs.
+
+Tolerances (stated with the method's target accuracy): bf16 outputs max-abs <= 2e-2 and
+mean-abs <= 2e-3, lse within 1e-3 absolute; -inf lse entries must match exactly.  Mask
+and offset handling is checked bit for bit.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gqa_attention_sink_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sink_amd as pkg
+    pkg.load()
+    return pkg
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _compare(out, lse, ref_out, ref_lse, what=""):
+    o = _np(out).reshape(ref_out.shape)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err = np.abs(o - ref_out)
+    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean-abs {err.mean():.3e}"
+    if lse is not None:
+        l = _np(lse).reshape(ref_lse.shape)
+        assert np.array_equal(np.isneginf(l), np.isneginf(ref_lse)), f"{what}: -inf lse pattern"
+        fin = np.isfinite(ref_lse)
+        if fin.any():
+            le = np.abs(l[fin] - ref_lse[fin]).max()
+            assert le <= LSE_TOL, f"{what}: lse err {le:.3e}"
+    return err.max(), err.mean()
+
+
+def _run_prefill(sa, w):
+    return sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q,
+                      w.scale, w.causal)
+
+
+def _oracle_prefill(w):
+    return oracle.sink_attention(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q.cpu(),
+                                 w.cu_seqlens_kv.cpu(), w.scale, w.causal)
+
+
+def _run_decode(sa, w, num_splits=None):
+    ns = w.num_splits if num_splits is None else num_splits
+    return sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, ns)
+
+
+def _oracle_decode(w):
+    return oracle.sink_attention_decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv.cpu(),
+                                        w.scale, w.causal)
+
+
+# ------------------------------------------------------------------ prefill
+def test_prefill_tiny_config(sa):
+    w = wl.make("tiny_prefill", device="cuda")
+    _say("tiny_prefill")
+    out, lse = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_prefill(w)
+    _compare(out, lse, ro, rl, "tiny_prefill")
+
+
+PREFILL_CASES = [
+    # lens_q, lens_kv, hq, hkv, d, sink, causal
+    ([1], [1], 4, 1, 64, ("normal", 0, 1), True),
+    ([5, 64, 65, 130], [5, 64, 65, 130], 8, 2, 64, ("normal", 0, 2), True),
+    ([200, 3, 77], [200, 3, 77], 6, 6, 128, ("normal", 0, 2), True),        # G=1
+    ([300, 129], [300, 129], 4, 2, 128, ("alt_neginf", 2, 1), True),        # G=2
+    ([100, 250], [100, 250], 6, 2, 64, ("normal", 0, 2), True),             # G=3
+    ([40, 70], [90, 33], 8, 2, 64, ("normal", 0, 2), False),                # non-causal
+    ([17, 64, 1], [100, 300, 65], 8, 1, 128, ("normal", 0, 2), True),       # cached prefix
+    ([150], [150], 8, 2, 64, None, True),                                   # no sinks
+    ([150], [150], 8, 2, 128, ("neginf", 0, 0), True),                      # all -inf
+    ([33, 97], [33, 97], 8, 2, 64, ("normal", 8, 1), True),                 # sink-dominant
+    ([300], [300], 64, 4, 128, ("alt_neginf", 2, 1), True),                 # long-prefill shape
+    ([257, 511], [257, 511], 64, 8, 64, ("normal", 0, 2), True),            # varlen shape
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_cases(sa, case):
+    lq, lk, hq, hkv, d, sink, causal = PREFILL_CASES[case]
+    _say(f"prefill case {case}: lq={lq} lk={lk} hq={hq} hkv={hkv} d={d} sink={sink} causal={causal}")
+    w = wl.make_prefill(lq, lk, hq, hkv, d, sink, 1 / math.sqrt(d), causal, seed=100 + case,
+                        device="cuda")
+    out, lse = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_prefill(w)
+    _compare(out, lse, ro, rl, f"prefill case {case}")
+
+
+def test_prefill_varlen_config_reduced(sa):
+    """The varlen workload's shape (8 sequences, Hq 64, Hkv 8, D 64) with shorter lengths
+    so the oracle checks every output."""
+    w = wl.make("varlen_prefill", device="cuda", lens=(64, 700))
+    _say(f"varlen reduced lens={w.lens_q}")
+    out, lse = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_prefill(w)
+    _compare(out, lse, ro, rl, "varlen reduced")
+
+
+def _sampled_prefill_check(sa, w, rows, what):
+    out, lse = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    cq = w.cu_seqlens_q.cpu().tolist()
+    ck = w.cu_seqlens_kv.cpu().tolist()
+    for b, i in rows:
+        lq = cq[b + 1] - cq[b]
+        lk = ck[b + 1] - ck[b]
+        i = min(i, lq - 1)
+        nk = i + (lk - lq) + 1 if w.causal else lk
+        qrow = w.q[cq[b] + i:cq[b] + i + 1]
+        kk = w.k[:, ck[b]:ck[b] + nk]
+        vv = w.v[:, ck[b]:ck[b] + nk]
+        ro, rl = oracle.sink_attention(qrow, kk, vv, w.sinks, [0, 1], [0, nk], w.scale, True)
+        _compare(out[cq[b] + i:cq[b] + i + 1], lse[cq[b] + i:cq[b] + i + 1], ro, rl,
+                 f"{what} b={b} i={i}")
+
+
+@pytest.mark.slow
+def test_prefill_varlen_full_sampled(sa):
+    w = wl.make("varlen_prefill", device="cuda")
+    _say(f"varlen full lens={w.lens_q}")
+    rows = [(b, i) for b in range(w.batch) for i in (0, 63, 64, 1000, 10 ** 6)]
+    _sampled_prefill_check(sa, w, rows, "varlen full")
+
+
+@pytest.mark.slow
+def test_prefill_long_full_sampled(sa):
+    w = wl.make("long_prefill", device="cuda")
+    _say("long_prefill full")
+    rows = [(0, i) for i in (0, 1, 63, 64, 255, 256, 2999, 4095, 5937, 5999)]
+    _sampled_prefill_check(sa, w, rows, "long full")
+
+
+# ------------------------------------------------------------------ decode
+def test_decode_config_full(sa):
+    """The gpt-oss-like decode workload at full size, every output checked."""
+    w = wl.make("decode_gptoss", device="cuda")
+    _say(f"decode_gptoss full sum_kv={sum(w.lens_kv)}")
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_decode(w)
+    _compare(out, lse, ro, rl, "decode_gptoss")
+
+
+DECODE_CASES = [
+    # lens_kv, q_len, hq, hkv, d, sink, causal, num_splits
+    ([1, 2, 31, 33, 64], 1, 8, 1, 64, ("normal", 0, 2), True, 0),
+    ([5, 40, 1000], 4, 16, 4, 128, ("normal", 0, 2), True, 0),
+    ([4, 100, 777], 3, 8, 2, 64, ("alt_neginf", 2, 1), True, 3),
+    ([129, 2049], 2, 64, 8, 64, ("normal", 0, 2), True, 64),
+    ([600, 300], 4, 64, 2, 128, ("normal", 0, 2), True, 5),      # 128 rows -> 2 row groups
+    ([512, 70], 1, 8, 8, 128, None, True, 1),                      # direct single chunk
+    ([90, 45], 4, 12, 4, 64, ("normal", 8, 1), False, 0),         # non-causal, sink-heavy
+    ([256, 1], 2, 4, 4, 128, ("neginf", 0, 0), True, 2),
+    ([3000], 4, 24, 4, 64, ("normal", 0, 2), True, 0),           # G=6: 24 rows, 2 n-tiles
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_decode_cases(sa, case):
+    lens, ql, hq, hkv, d, sink, causal, ns = DECODE_CASES[case]
+    _say(f"decode case {case}: lens={lens} q_len={ql} hq={hq} hkv={hkv} d={d} ns={ns}")
+    w = wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, ns,
+                       seed=200 + case, device="cuda")
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_decode(w)
+    _compare(out, lse, ro, rl, f"decode case {case}")
+
+
+@pytest.mark.slow
+def test_decode_spec_full_sampled(sa):
+    """Speculative decode at full size (256 x 32768 keys, 32 chunks); the oracle checks
+    three whole sequences (every token and head)."""
+    w = wl.make("spec_decode", device="cuda")
+    _say("spec_decode full")
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ind = w.cu_seqlens_kv.cpu().tolist()
+    for b in (0, 137, 255):
+        ks = slice(ind[b], ind[b + 1])
+        ro, rl = oracle.sink_attention_decode(w.q[b:b + 1], w.k[:, ks], w.v[:, ks], w.sinks,
+                                              [0, ind[b + 1] - ind[b]], w.scale, w.causal)
+        _compare(out[b:b + 1], lse[b:b + 1], ro, rl, f"spec_decode b={b}")
+
+
+@pytest.mark.parametrize("ns", [0, 4, 7])
+def test_decode_partials_match_oracle_chunks(sa, ns):
+    """Per-chunk partials of the split kernel against the oracle's chunk form with the
+    same chunk plan: checks the planner, the sink in chunk 0 only and empty chunks."""
+    lens = [1, 40, 600, 2000, 5000]
+    w = wl.make_decode(lens, 2, 16, 4, 64, ("normal", 1, 2), 0.125, True, ns, seed=300 + ns,
+                       device="cuda")
+    _say(f"partials ns={ns}")
+    po, pl = sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                               True, ns)
+    torch.cuda.synchronize()
+    s = pl.shape[1]
+    bounds = []
+    for lk in lens:
+        bd = oracle.plan_chunks(lk, ns)
+        bounds.append(bd + [lk] * (s + 1 - len(bd)))
+    cu_q = torch.arange(len(lens) + 1, dtype=torch.int32) * 2
+    q2 = w.q.reshape(-1, 16, 64)
+    _, _, ref_po, ref_pl = oracle.sink_attention_chunked(q2, w.k, w.v, w.sinks, cu_q,
+                                                         w.cu_seqlens_kv.cpu(), w.scale, True,
+                                                         bounds, return_partials=True)
+    ref_pl = ref_pl.reshape(-1, s)
+    ref_po = ref_po.reshape(-1, s, 64)
+    gl = _np(pl)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(ref_pl)), "empty-chunk pattern"
+    fin = np.isfinite(ref_pl)
+    assert np.abs(gl[fin] - ref_pl[fin]).max() <= LSE_TOL
+    go = _np(po)
+    err = np.abs(go[fin] - ref_po[fin])
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+
+
+def test_merge_against_oracle(sa):
+    g = torch.Generator().manual_seed(7)
+    rows, s, d = 300, 9, 128
+    po = torch.randn(rows, s, d, generator=g)
+    pl = torch.randn(rows, s, generator=g) * 3
+    pl[torch.rand(rows, s, generator=g) < 0.3] = float("-inf")
+    pl[5] = float("-inf")
+    _say("merge")
+    out, lse = sa.merge(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_partials(po, pl)
+    _compare(out, lse, ro, rl, "merge")
+    assert torch.all(out[5] == 0) and torch.isneginf(lse[5])
+
+
+def test_decode_split_invariance(sa):
+    w = wl.make_decode([700, 3000, 64], 4, 16, 2, 128, ("normal", 0, 2), 1 / math.sqrt(128),
+                       True, 0, seed=400, device="cuda")
+    _say("split invariance")
+    ro, rl = _oracle_decode(w)
+    for ns in (1, 0, 2, 32, 64):
+        out, lse = _run_decode(sa, w, ns)
+        torch.cuda.synchronize()
+        _compare(out, lse, ro, rl, f"num_splits={ns}")
+
+
+# ------------------------------------------------------------------ bit-exact properties
+def test_prefill_masked_positions_bitwise(sa):
+    w = wl.make_prefill([70, 130], [70, 130], 8, 2, 64, ("normal", 0, 2), 0.125, True,
+                        seed=500, device="cuda")
+    _say("prefill masked perturbation")
+    o1, l1 = _run_prefill(sa, w)
+    last = int(w.cu_seqlens_kv[2].item()) - 1          # visible to the last row only
+    w.k[:, last] = 3.0
+    w.v[:, last] = -5.0
+    o2, l2 = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:-1], o2[:-1]) and torch.equal(l1[:-1], l2[:-1])
+    assert not torch.equal(o1[-1], o2[-1])
+
+
+def test_prefill_nan_past_end_and_packing_bitwise(sa):
+    """NaN-filled key/value storage after the last sequence never leaks; a sequence
+    packed after others is bitwise identical to the same sequence run alone."""
+    lens = [37, 200, 129]
+    w = wl.make_prefill(lens, lens, 8, 2, 128, ("normal", 0, 2), 0.1, True, seed=501,
+                        device="cuda")
+    _say("prefill nan tail / packing")
+    o1, l1 = _run_prefill(sa, w)
+    tk = w.k.shape[1]
+    pad = 300
+    kp = torch.full((2, tk + pad, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    kp[:, :tk] = w.k
+    vp[:, :tk] = w.v
+    o2, l2 = sa.prefill(w.q, kp, vp, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q,
+                        w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # sequence 1 alone
+    a, bnd = 37, 237
+    cu = torch.tensor([0, 200], dtype=torch.int32, device="cuda")
+    o3, l3 = sa.prefill(w.q[a:bnd].contiguous(), w.k[:, a:bnd].contiguous(),
+                        w.v[:, a:bnd].contiguous(), w.sinks, cu, cu, 200, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1[a:bnd]) and torch.equal(l3, l1[a:bnd])
+
+
+def test_decode_nan_past_end_and_packing_bitwise(sa):
+    lens = [100, 1500, 33]
+    w = wl.make_decode(lens, 4, 16, 2, 64, ("normal", 0, 2), 0.125, True, 6, seed=502,
+                       device="cuda")
+    _say("decode nan tail / packing")
+    o1, l1 = _run_decode(sa, w)
+    tk = w.k.shape[1]
+    kp = torch.full((2, tk + 64, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    kp[:, :tk] = w.k
+    vp[:, :tk] = w.v
+    o2, l2 = sa.decode(w.q, kp, vp, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, True, 6)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ind = torch.tensor([0, 1500], dtype=torch.int32, device="cuda")
+    o3, l3 = sa.decode(w.q[1:2].contiguous(), w.k[:, 100:1600].contiguous(),
+                       w.v[:, 100:1600].contiguous(), w.sinks, ind, 1500, w.scale, True, 6)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1[1:2]) and torch.equal(l3, l1[1:2])
+
+
+def test_decode_draft_mask_bitwise(sa):
+    """Causal within the draft: the last key is visible only to the last draft token."""
+    w = wl.make_decode([300, 64], 4, 8, 2, 128, ("normal", 0, 2), 0.09, True, 3, seed=503,
+                       device="cuda")
+    _say("decode draft mask")
+    o1, l1 = _run_decode(sa, w)
+    last = int(w.cu_seqlens_kv[1].item()) - 1
+    w.k[:, last] = 2.5
+    w.v[:, last] = 9.0
+    o2, l2 = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0, :3], o2[0, :3]) and torch.equal(l1[0, :3], l2[0, :3])
+    assert torch.equal(o1[1], o2[1])
+    assert not torch.equal(o1[0, 3], o2[0, 3])
+
+
+def test_determinism(sa):
+    w = wl.make_prefill([333, 64], [333, 64], 16, 2, 128, ("normal", 0, 2), 0.09, True,
+                        seed=504, device="cuda")
+    d = wl.make_decode([900, 4000], 4, 16, 4, 128, ("normal", 0, 2), 0.09, True, 0, seed=505,
+                       device="cuda")
+    _say("determinism")
+    a1 = _run_prefill(sa, w)
+    a2 = _run_prefill(sa, w)
+    b1 = _run_decode(sa, d)
+    b2 = _run_decode(sa, d)
+    torch.cuda.synchronize()
+    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+    assert torch.equal(b1[0], b2[0]) and torch.equal(b1[1], b2[1])

@@ -5,8 +5,9 @@
 One step is one pass of the whole decode hot path (split-KV kernel + log-sum-exp
 merge) over the gpt-oss-like decode batch (64 sequences, 1 query token, Hq 64 over
 Hkv 8, head_dim 64, KV lengths uniform in [1024, 8192]), with inputs resident in HBM.
-Before every step a 512 MiB write evicts the 256 MB Infinity Cache and the L2s, so
-each step streams its K/V from HBM; only the attention kernels sit inside the timed
+Before every step a 512 MiB read (a sum over a scratch buffer) evicts the 256 MB
+Infinity Cache and the L2s with clean lines, so each step streams its K/V from HBM and
+pays no write-back of dirty lines; only the attention kernels sit inside the timed
 event pair.  The line also reports the other workloads (varlen and long prefill in
 TFLOP/s, speculative decode in GB/s) and the fp64 CPU oracle on a bounded sample.
 
@@ -110,14 +111,14 @@ def bench_decode(sa, w, steps, warmup, flush):
     pl = torch.empty((rows, s), dtype=torch.float32, device="cuda")
 
     def step_full(t=None, i=0):
-        flush.zero_()
+        flush.sum()
         if t: t.mark(i, 0)
         sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal,
                   w.num_splits, workspace=ws, out=out, lse=lse)
         if t: t.mark(i, 1)
 
     def step_split(t, i):
-        flush.zero_()
+        flush.sum()
         t.mark(i, 0)
         sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
                           w.causal, w.num_splits, part_o=po, part_lse=pl)
@@ -152,7 +153,7 @@ def bench_prefill(sa, w, steps, warmup, flush):
     lse = torch.empty((w.q.shape[0], w.hq), dtype=torch.float32, device="cuda")
 
     def step(t=None, i=0):
-        flush.zero_()
+        flush.sum()
         if t: t.mark(i, 0)
         sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q, w.scale,
                    w.causal, out=out, lse=lse)
@@ -211,6 +212,9 @@ def main():
     ap.add_argument("--workload", default="decode_gptoss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the reference "
+                         "kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -221,6 +225,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
+
     import gqa_attention_sink_amd as sa
     from gqa_attention_sink_amd import workloads as wl
     if not os.path.exists(sa.LIB_PATH):
@@ -228,7 +242,7 @@ def main():
         build()
     sa.load()
     torch.cuda.set_device(0)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     _say(f"workload {args.workload}")
     w = wl.make(args.workload, device="cuda")

@@ -72,7 +72,9 @@ sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const fl
   a.q_len = q_len;
   a.num_q_heads = hq;
   a.group = hq / hkv;
-  a.row_groups = (q_len * a.group + 63) / 64;
+  const int rows = q_len * a.group;
+  const int w = sa::decode_waves(rows);
+  a.row_groups = (rows + 16 * w - 1) / (16 * w);
   a.num_splits = num_splits;
   a.num_slots = planned_slots(max_kv_len, num_splits);
   a.causal = causal;

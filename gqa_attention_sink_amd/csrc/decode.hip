@@ -7,16 +7,17 @@
 // (sink, 1) and every other chunk from (-inf, 0); the merge then combines the chunks
 // by their log-sum-exp.
 //
-// One wavefront owns one (sequence, KV head, row group, chunk).  The q_len * G query
+// One workgroup owns one (sequence, KV head, row group, chunk).  The q_len * G query
 // rows that share the KV head (GQA) are the N dimension of the MFMAs, so each K/V byte
 // is read from HBM once per KV head.  Scores are computed transposed, S^T = K . Q^T,
 // with v_mfma_f32_16x16x32_bf16: the accumulator of S^T leaves every lane holding
 // scores of ONE query row, which is exactly the B-operand layout of the next product
 // O^T = V^T . P^T, so probabilities never leave registers and the per-row softmax
-// state (m, d, rescale) is lane-local.  K and V stream straight from HBM into
-// registers with bounded 16-byte buffer loads; V is transposed in registers.
+// state (m, d, rescale) is lane-local.  K and V stream from HBM through
+// an LDS ring with asynchronous buffer->LDS copies; V is transposed in registers.
 #include "sa_device.h"
 #include "sa_kernels.h"
+
 
 namespace sa {
 
@@ -37,13 +38,36 @@ __device__ __forceinline__ int slot_key(int cg, int i) {
   return (i < 4) ? (4 * cg + i) : (16 + 4 * cg + (i - 4));
 }
 
-template <int D, int NT, bool DIRECT>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  constexpr int KS = D / 32;   // k-steps (32 head dims each) of S^T
-  constexpr int DPL = D / 16;  // head dims per lane in a V row load = d-tiles of O^T
-  constexpr int ROW_BYTES = D * 2;
+// XOR swizzle of 16-byte chunks inside a K row in LDS: the 16 rows read by one MFMA
+// operand load land in distinct banks.
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
 
-  const int lane = threadIdx.x;
+// Decode split kernel.  Workgroup = W wavefronts = one (sequence, KV head, row group,
+// chunk); wavefront w owns 16 query rows.  The chunk's K and V stream from HBM into an
+// NST-stage LDS ring with asynchronous 16-byte buffer->LDS copies (no registers),
+// NST-1 stages ahead of the compute, and every wavefront reads each stage from LDS.
+template <int D, int W, bool DIRECT>
+__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;              // k-steps (32 head dims) of S^T
+  constexpr int DPL = D / 16;             // head dims per lane per V row read = O^T d-tiles
+  constexpr int ROW = D * 2;              // bytes per K/V row
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int STEP = 32;                // keys per stage
+  // LDS ring stages: deeper rings cost workgroups per CU (fewer wavefronts to issue
+  // copies), which measured slower; 3 stages for head_dim 64, 4 for 128.
+  constexpr int NST = (D == 64) ? 3 : 4;
+  constexpr int SB = STEP * ROW;          // bytes of K (or V) per stage
+  constexpr int NDMA = SB / (64 * W * 16);  // copies per thread per tensor per stage
+  static_assert(NDMA * 64 * W * 16 == SB, "stage must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NST][2][SB];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int l16 = lane & 15;
   const int cg = lane >> 4;
   const int c = blockIdx.x;
@@ -60,148 +84,147 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int cl = chunk_len(lk, n);
   const int S = a.num_slots;
 
-  // Rows owned by this lane, one per n-tile.
-  int row_t[NT], row_h[NT];
-  bool row_ok[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int R = rg * 64 + nt * 16 + l16;
-    row_t[nt] = R / G;
-    row_h[nt] = blockIdx.y / a.row_groups * G + (R - row_t[nt] * G);
-    row_ok[nt] = R < M;
-  }
+  // The lane's query row: R -> (draft token t, query head h).
+  const int R = rg * 16 * W + wave * 16 + l16;
+  const int row_t = R / G;
+  const int row_h = g * G + (R - row_t * G);
+  const bool row_ok = R < M;
+  const int64_t qrow = ((int64_t)b * a.q_len + row_t) * Hq + row_h;
 
   if (c >= n) {  // unused slot: no mass
-    if (!DIRECT && cg == 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (row_ok[nt]) {
-          const int64_t qrow = ((int64_t)b * a.q_len + row_t[nt]) * Hq + row_h[nt];
-          a.part_lse[qrow * S + c] = kNegInf;
-        }
-    }
+    if (!DIRECT && cg == 0 && row_ok) a.part_lse[qrow * S + c] = kNegInf;
     return;
   }
   const int kb = min(lk, c * cl);
   const int ke = min(lk, kb + cl);
+  const int nsteps = (ke - kb + STEP - 1) / STEP;
 
-  // Q^T operands (B of S^T): lane holds Q[row][ks*32 + cg*8 .. +8].
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(
-      (const __bf16*)a.q + (size_t)b * a.q_len * Hq * D, (uint32_t)(a.q_len * Hq * ROW_BYTES));
-  bf16x8 qop[NT][KS];
+  // K/V of this chunk: loads past the chunk end return zero.
+  const size_t head_base = ((size_t)g * a.total_kv + kv0 + kb) * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, (uint32_t)(ke - kb) * ROW);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, (uint32_t)(ke - kb) * ROW);
+  auto issue = [&](int st) {
+    unsigned char* kbuf = ring[st % NST][0];
+    unsigned char* vbuf = ring[st % NST][1];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // rows past M have row_t >= q_len (or a padded head): zero via the bound, or
-      // explicitly for padded heads of the last token.
-      const uint32_t off = (uint32_t)((row_t[nt] * Hq + row_h[nt]) * ROW_BYTES + (ks * 32 + cg * 8) * 2);
-      u32x4 v = load16(qr, row_ok[nt] ? off : 0xFFFFFFF0u);
-      qop[nt][ks] = as_bf16x8(v);
+    for (int i = 0; i < NDMA; ++i) {
+      const int blk = i * W + wave;           // 1 KiB block of the stage this wave fills
+      const int p = blk * 64 + lane;          // 16-byte chunk index inside the stage
+      const int row = p / CPR;
+      const int cc = p - row * CPR;
+      const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
+      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
     }
+  };
 
-  // Online-softmax state in log2 units; the sink joins chunk 0 only.
-  float m[NT], dsum[NT];
+  // Q^T operands (B of S^T): lane holds Q[row][ks*32 + cg*8 .. +8]; zero for padding.
+  const uint32_t qbytes = (uint32_t)(a.q_len * Hq * ROW);
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc((const __bf16*)a.q + (size_t)b * a.q_len * Hq * D, qbytes);
+  bf16x8 qop[KS];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float sig = kNegInf;
-    if (c == 0 && a.sinks != nullptr && row_ok[nt]) sig = a.sinks[row_h[nt]] * kLog2e;
-    m[nt] = sig;
-    dsum[nt] = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;  // counted once per row
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)((row_t * Hq + row_h) * ROW + (ks * 32 + cg * 8) * 2);
+    qop[ks] = as_bf16x8(load16(qr, row_ok ? off : qbytes));
   }
-  f32x4 o[DPL][NT];
+  // Online-softmax state in log2 units; the sink joins chunk 0 only and is counted by
+  // one lane of the four that share a row.
+  float sig = kNegInf;
+  if (c == 0 && a.sinks != nullptr && row_ok) sig = a.sinks[row_h] * kLog2e;
+  float m = sig;
+  float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;
+  f32x4 o[DPL];
 #pragma unroll
-  for (int t = 0; t < DPL; ++t)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < DPL; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t head_base = ((size_t)g * a.total_kv + kv0) * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, (uint32_t)lk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, (uint32_t)lk * ROW_BYTES);
   const float sl2 = a.scale_log2;
   const int causal_first_masked = a.causal ? (lk - a.q_len + 1) : 0x7fffffff;
+  const int lim = min(ke - 1, a.causal ? lk - a.q_len + row_t : 0x7fffffff);
 
-  for (int kbase = kb; kbase < ke; kbase += 32) {
-    // ---- K operands (A of S^T): K[key = kbase + kt*16 + l16][ks*32 + cg*8 .. +8]
-    u32x4 kop[2][KS];
+  // Stages are issued unconditionally: a stage past the chunk end reads zeros through
+  // the bounded descriptor (no memory traffic), which keeps the copy count per stage
+  // constant so one fixed wait suffices.
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+  for (int st = 0; st < NST - 1; ++st) issue(st);
+
+  for (int st = 0; st < nsteps; ++st) {
+    // stage st has landed once only the NST-2 stages issued after it are pending
+    wait_vmcnt<((NST - 2) * 2 * NDMA < 63 ? (NST - 2) * 2 * NDMA : 63)>();
+    __syncthreads();
+    issue(st + NST - 1);  // refills the slot every wavefront finished with (st-1)
+
+    const unsigned char* kbuf = ring[st % NST][0];
+    const unsigned char* vbuf = ring[st % NST][1];
+    const int kbase = kb + st * STEP;
+
+    // ---- S^T = K . Q^T for two 16-key tiles
+    f32x4 s2[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kop[kt][ks] = load16(kr, (uint32_t)(kbase + kt * 16 + l16) * ROW_BYTES + (ks * 32 + cg * 8) * 2);
-    // ---- V rows: lane reads DPL head dims [DPL*l16, +DPL) of the 8 keys of its slots
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int row = kt * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *(const u32x4*)(kbuf + row * ROW + (((ks * 4 + cg) ^ dswz<D>(row)) * 16));
+        acc = mfma16(as_bf16x8(kv), qop[ks], acc);
+      }
+      s2[kt] = acc;
+    }
+    // ---- mask: keys past the chunk end, and (causal) keys after the row's position
+    if (kbase + STEP > ke || kbase + STEP > causal_first_masked) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kbase + kt * 16 + 4 * cg + j;
+          s2[kt][j] = (key <= lim) ? s2[kt][j] : kNegInf;
+        }
+    }
+    // ---- online softmax; the running max is raised only when a row's max grows by
+    // more than 2^8 (exact: numerator and denominator share the stale max)
+    float mx = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                     fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float mxs = mx * sl2;
+    if (__any(mxs > m + 8.0f)) {
+      const float mnew = fmaxf(m, mxs);
+      const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+      dsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) o[t] *= alpha;
+      m = mnew;
+    }
+    const float msub = (m == kNegInf) ? 0.0f : m;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(__builtin_fmaf(s2[0][j], sl2, -msub));
+      p[4 + j] = fast_exp2(__builtin_fmaf(s2[1][j], sl2, -msub));
+    }
+    dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    u32x4 pk;
+    pk.x = pack_bf16x2(p[0], p[1]);
+    pk.y = pack_bf16x2(p[2], p[3]);
+    pk.z = pack_bf16x2(p[4], p[5]);
+    pk.w = pack_bf16x2(p[6], p[7]);
+    const bf16x8 pop = as_bf16x8(pk);
+
+    // ---- O^T += V^T . P^T.  V row of slot key i, head dims [DPL*l16, +DPL); d-tile t
+    // of the MFMA holds head dim DPL*m + t in row m.
     uint32_t vw[8][DPL / 2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t off = (uint32_t)(kbase + slot_key(cg, i)) * ROW_BYTES + l16 * DPL * 2;
+      const unsigned char* src = vbuf + slot_key(cg, i) * ROW + l16 * DPL * 2;
       if constexpr (DPL == 8) {
-        u32x4 t4 = load16(vr, off);
+        const u32x4 t4 = *(const u32x4*)src;
         vw[i][0] = t4.x; vw[i][1] = t4.y; vw[i][2] = t4.z; vw[i][3] = t4.w;
       } else {
-        u32x2 t2 = load8(vr, off);
+        const u32x2 t2 = *(const u32x2*)src;
         vw[i][0] = t2.x; vw[i][1] = t2.y;
       }
     }
-
-    // ---- S^T = K . Q^T
-    f32x4 s[2][NT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(as_bf16x8(kop[kt][ks]), qop[nt][ks], acc);
-        s[kt][nt] = acc;
-      }
-
-    // ---- mask: keys past the chunk end, and (causal) keys after the row's position.
-    if (kbase + 32 > ke || kbase + 32 > causal_first_masked) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int lim = a.causal ? min(ke - 1, lk - a.q_len + row_t[nt]) : ke - 1;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kbase + kt * 16 + 4 * cg + j;
-            s[kt][nt][j] = (key <= lim) ? s[kt][nt][j] : kNegInf;
-          }
-      }
-    }
-
-    // ---- online softmax (exp2 domain) and P^T operands
-    bf16x8 pop[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = fmaxf(fmaxf(fmaxf(s[0][nt][0], s[0][nt][1]), fmaxf(s[0][nt][2], s[0][nt][3])),
-                       fmaxf(fmaxf(s[1][nt][0], s[1][nt][1]), fmaxf(s[1][nt][2], s[1][nt][3])));
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
-      const float mnew = fmaxf(m[nt], mx * sl2);
-      const bool dead = (mnew == kNegInf);
-      const float alpha = dead ? 1.0f : fast_exp2(m[nt] - mnew);
-      const float msub = dead ? 0.0f : mnew;
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = fast_exp2(__builtin_fmaf(s[0][nt][j], sl2, -msub));
-        p[4 + j] = fast_exp2(__builtin_fmaf(s[1][nt][j], sl2, -msub));
-      }
-      float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      dsum[nt] = __builtin_fmaf(dsum[nt], alpha, ps);
-      m[nt] = mnew;
-#pragma unroll
-      for (int t = 0; t < DPL; ++t) o[t][nt] *= alpha;
-      u32x4 pk;
-      pk.x = pack_bf16x2(p[0], p[1]);
-      pk.y = pack_bf16x2(p[2], p[3]);
-      pk.z = pack_bf16x2(p[4], p[5]);
-      pk.w = pack_bf16x2(p[6], p[7]);
-      pop[nt] = as_bf16x8(pk);
-    }
-
-    // ---- O^T += V^T . P^T ; V^T operand of d-tile t holds V[slot key i][DPL*l16 + t]
 #pragma unroll
     for (int t = 0; t < DPL; ++t) {
       u32x4 va;
@@ -217,47 +240,43 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         va.z = hi_hi(vw[4][w], vw[5][w]);
         va.w = hi_hi(vw[6][w], vw[7][w]);
       }
-      const bf16x8 vop = as_bf16x8(va);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[t][nt] = mfma16(vop, pop[nt], o[t][nt]);
+      o[t] = mfma16(as_bf16x8(va), pop, o[t]);
     }
   }
 
-  // ---- epilogue: lane holds head dims [4*cg*DPL, 4*cg*DPL + 4*DPL) of its row;
-  // O^T accumulator element (t, j) is head dim DPL*(4*cg + j) + t.
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+
+  // ---- epilogue: lane holds head dims [4*cg*DPL, +4*DPL) of its row; O^T element
+  // (t, j) is head dim DPL*(4*cg + j) + t.
+  float dr = wave_xor_sum(dsum, 16);
+  dr = wave_xor_sum(dr, 32);
+  if (!row_ok) return;
+  const float inv = dr > 0.f ? 1.0f / dr : 0.f;
+  const float lse_nat = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
+  float vals[4 * DPL];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float dr = wave_xor_sum(dsum[nt], 16);
-    dr = wave_xor_sum(dr, 32);
-    const float inv = dr > 0.f ? 1.0f / dr : 0.f;
-    const float lse_nat = dr > 0.f ? (m[nt] + __builtin_log2f(dr)) * kLn2 : kNegInf;
-    if (!row_ok[nt]) continue;
-    const int64_t qrow = ((int64_t)b * a.q_len + row_t[nt]) * Hq + row_h[nt];
-    float vals[4 * DPL];
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int t = 0; t < DPL; ++t) vals[j * DPL + t] = o[t][j] * inv;
+  const int d0 = 4 * cg * DPL;
+  if constexpr (DIRECT) {
+    uint32_t* dst = (uint32_t*)((__bf16*)a.out + qrow * D + d0);
 #pragma unroll
-      for (int t = 0; t < DPL; ++t) vals[j * DPL + t] = o[t][nt][j] * inv;
-    const int d0 = 4 * cg * DPL;
-    if constexpr (DIRECT) {
-      uint32_t* dst = (uint32_t*)((__bf16*)a.out + qrow * D + d0);
-#pragma unroll
-      for (int e = 0; e < 4 * DPL; e += 8) {
-        u32x4 w4;
-        w4.x = pack_bf16x2(vals[e + 0], vals[e + 1]);
-        w4.y = pack_bf16x2(vals[e + 2], vals[e + 3]);
-        w4.z = pack_bf16x2(vals[e + 4], vals[e + 5]);
-        w4.w = pack_bf16x2(vals[e + 6], vals[e + 7]);
-        *(u32x4*)(dst + e / 2) = w4;
-      }
-      if (cg == 0 && a.lse != nullptr) a.lse[qrow] = lse_nat;
-    } else {
-      float* dst = a.part_o + (qrow * S + c) * D + d0;
-#pragma unroll
-      for (int e = 0; e < 4 * DPL; e += 4)
-        *(f32x4*)(dst + e) = f32x4{vals[e], vals[e + 1], vals[e + 2], vals[e + 3]};
-      if (cg == 0) a.part_lse[qrow * S + c] = lse_nat;
+    for (int e = 0; e < 4 * DPL; e += 8) {
+      u32x4 w4;
+      w4.x = pack_bf16x2(vals[e + 0], vals[e + 1]);
+      w4.y = pack_bf16x2(vals[e + 2], vals[e + 3]);
+      w4.z = pack_bf16x2(vals[e + 4], vals[e + 5]);
+      w4.w = pack_bf16x2(vals[e + 6], vals[e + 7]);
+      *(u32x4*)(dst + e / 2) = w4;
     }
+    if (cg == 0 && a.lse != nullptr) a.lse[qrow] = lse_nat;
+  } else {
+    float* dst = a.part_o + (qrow * S + c) * D + d0;
+#pragma unroll
+    for (int e = 0; e < 4 * DPL; e += 4)
+      *(f32x4*)(dst + e) = f32x4{vals[e], vals[e + 1], vals[e + 2], vals[e + 3]};
+    if (cg == 0) a.part_lse[qrow * S + c] = lse_nat;
   }
 }
 
@@ -299,26 +318,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }
 
 template <int D, bool DIRECT>
-static hipError_t launch_decode_d(const DecodeArgs& a, int nt, dim3 grid, hipStream_t st) {
-  switch (nt) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int w, dim3 grid, hipStream_t st) {
+  switch (w) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, DIRECT>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT>), grid, dim3(64), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3, DIRECT>), grid, dim3(64), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT>), grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT>), grid, dim3(256), 0, st, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
                                bool direct, hipStream_t stream) {
-  const int M = a.q_len * a.group;
-  const int nt = a.row_groups > 1 ? 4 : (M + 15) / 16;
+  const int w = decode_waves(a.q_len * a.group);
   dim3 grid(a.num_slots, num_kv_heads * a.row_groups, batch);
   if (head_dim == 64)
-    return direct ? launch_decode_d<64, true>(a, nt, grid, stream)
-                  : launch_decode_d<64, false>(a, nt, grid, stream);
-  return direct ? launch_decode_d<128, true>(a, nt, grid, stream)
-                : launch_decode_d<128, false>(a, nt, grid, stream);
+    return direct ? launch_decode_d<64, true>(a, w, grid, stream)
+                  : launch_decode_d<64, false>(a, w, grid, stream);
+  return direct ? launch_decode_d<128, true>(a, w, grid, stream)
+                : launch_decode_d<128, false>(a, w, grid, stream);
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows, int num_slots,

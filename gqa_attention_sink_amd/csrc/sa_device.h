@@ -38,6 +38,20 @@ __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// Asynchronous 16-byte copy global -> LDS (no registers): lane i of the wavefront
+// writes its 16 bytes at lds_wave_base + 16*i.  lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // D(16x16, fp32) += A(16x32) * B(32x16), bf16 inputs.

@@ -37,7 +37,7 @@ struct DecodeArgs {
   int32_t q_len;
   int32_t num_q_heads;
   int32_t group;       // query heads per KV head
-  int32_t row_groups;  // ceil(q_len * group / 64)
+  int32_t row_groups;  // ceil(q_len * group / (16 * decode_waves(q_len * group)))
   int32_t num_splits;  // 0 = planner
   int32_t num_slots;   // chunk slots per row in the partial layout
   int32_t causal;
@@ -47,6 +47,9 @@ struct DecodeArgs {
   void* out;           // [rows, D] bf16         (direct mode: one chunk per sequence)
   float* lse;          // [rows]
 };
+
+// Wavefronts per decode workgroup (16 query rows each) for M rows sharing a KV head.
+inline int decode_waves(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
                           hipStream_t stream);

@@ -132,9 +132,9 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
     a.num_q_heads = num_q_heads;
     a.group = num_q_heads / num_kv_heads;
     a.hg = heads_per_wg(a.group);
-    a.pw = 4 / a.hg;
+    a.pw = 8 / a.hg;
     a.n_hgroups = a.group / a.hg;
-    a.n_qtiles = (max_seqlen_q + 64 * a.pw - 1) / (64 * a.pw);
+    a.n_qtiles = (max_seqlen_q + 32 * a.pw - 1) / (32 * a.pw);
     a.causal = causal;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.out = out;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NST][2][SB];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int cg = lane >> 4;

@@ -5,18 +5,21 @@
 // the whole key range of a row is handled by one wavefront, so the sink is counted
 // exactly once.
 //
-// Work unit (one workgroup of 4 wavefronts): one sequence, 64*pw query positions and
-// hg query heads that share one KV head (GQA), hg*pw = 4.  Each wavefront owns 64
-// query rows of one head (two 32-row MFMA column tiles).  K/V tiles of 64 keys are
-// staged in LDS once per workgroup and read by all four wavefronts; the next tile's
-// global loads are issued before the current tile is computed.
+// Work unit (one workgroup of 8 wavefronts, two per SIMD): one sequence, 32*pw query
+// positions and hg query heads that share one KV head (GQA), hg*pw = 8.  Each
+// wavefront owns 32 query rows of one head (one 32-row MFMA column tile); the two
+// wavefronts of a SIMD overlap one's exponentials with the other's MFMAs.
 //
 // Scores are computed transposed, S^T = K . Q^T (v_mfma_f32_32x32x16_bf16), so each
 // lane holds scores of one query row: the P^T accumulator is directly the B operand
-// of O^T = V^T . P^T and the per-row softmax state is lane-local (one cross-lane max
-// per tile between the two lanes of a row).  V^T operands are assembled from 8-byte
-// LDS reads of 8 key rows and a register transpose.  Workgroups are dispatched
-// heaviest causal tile first.
+// of O^T = V^T . P^T and the per-row softmax state is lane-local (one swap of the
+// wavefront's 32-lane halves per row max).
+//
+// Keys are processed in units of 64.  K/V units stream through a 4-slot LDS ring with
+// asynchronous buffer->LDS copies issued 3 units ahead.  The running maximum is
+// raised only when a row's maximum grows by more than 2^8 (exact: numerator and
+// denominator share the stale maximum), so O is rarely rescaled.  Workgroups are
+// dispatched heaviest causal tile first.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -24,13 +27,17 @@ namespace sa {
 
 template <int D>
 struct PrefillCfg {
-  static constexpr int BC = 64;          // keys per tile
-  static constexpr int KS = D / 16;      // k-steps of S^T (16 head dims each)
-  static constexpr int DT = D / 32;      // d-tiles of O^T (32 head dims each)
-  static constexpr int CPR = D / 8;      // 16-byte chunks per K/V row
-  static constexpr int ROW = D * 2;      // bytes per K/V row
-  static constexpr int TILE = BC * ROW;  // bytes per K (or V) tile
-  static constexpr int NLD = BC * CPR / 256;  // 16-byte loads per thread per tensor
+  static constexpr int UNIT = 64;              // keys per pipeline unit
+  static constexpr int KS = D / 16;            // k-steps of S^T (16 head dims each)
+  static constexpr int DT = D / 32;            // d-tiles of O^T (32 head dims each)
+  static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+  static constexpr int ROW = D * 2;            // bytes per K/V row
+  static constexpr int UB = UNIT * ROW;        // bytes of K (or V) per unit
+  static constexpr int NS = 4;                 // LDS ring slots
+  static constexpr int PD = NS - 1;            // units issued ahead of use
+  static constexpr int NT = 512;               // threads per workgroup (8 wavefronts)
+  static constexpr int NDMA = UB / (NT * 16);  // copies per thread per tensor per unit
+  static_assert(NDMA * NT * 16 == UB, "unit must split evenly over the workgroup");
 };
 
 // XOR swizzle of 16-byte chunks inside a K row so that the 32 rows read by one MFMA
@@ -42,13 +49,12 @@ __device__ __forceinline__ int kswz(int row) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[C::TILE];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[C::TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[C::NS][2][C::UB];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int cg = lane >> 5;
@@ -64,169 +70,147 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int lq = a.cu_q[b + 1] - q0;
   const int kv0 = a.cu_kv[b];
   const int lk = a.cu_kv[b + 1] - kv0;
-  const int wg_p0 = qt * 64 * a.pw;
+  const int wg_p0 = qt * 32 * a.pw;
   if (wg_p0 >= lq) return;
   const int off = lk - lq;  // bottom-right causal alignment
 
+  // wavefront -> (query head, block of 32 query positions)
   const bool active = (wave / a.hg) < a.pw;
   const int h = g * a.group + hgrp * a.hg + (wave % a.hg);
-  const int p0 = wg_p0 + (wave / a.hg) * 64;
-
-  int kend_wg = a.causal ? min(lk, wg_p0 + 64 * a.pw + off) : lk;
-  kend_wg = max(kend_wg, 0);
-  const int ntiles = (kend_wg + C::BC - 1) / C::BC;
-  int kend_w = a.causal ? min(lk, p0 + 64 + off) : lk;
-  kend_w = max(kend_w, 0);
+  const int p0 = wg_p0 + (wave / a.hg) * 32;
   const bool has_rows = active && p0 < lq;
 
-  // ---- Q^T operands: lane holds Q[p0 + nt*32 + l32][h][ks*16 + cg*8 .. +8]
-  bf16x8 qop[2][C::KS];
+  int kend_wg = a.causal ? min(lk, wg_p0 + 32 * a.pw + off) : lk;
+  kend_wg = max(kend_wg, 0);
+  const int n_wg = (kend_wg + C::UNIT - 1) / C::UNIT;
+  int kend_w = a.causal ? min(lk, p0 + 32 + off) : lk;
+  kend_w = has_rows ? max(kend_w, 0) : 0;
+  const int n_w = (kend_w + C::UNIT - 1) / C::UNIT;
+
+  // ---- K/V of this (KV head, sequence) through bounded descriptors: units past the
+  // sequence end read zeros and cost no memory traffic.
+  const size_t head_base = ((size_t)g * a.total_kv + kv0) * D;
+  const uint32_t kvbytes = (uint32_t)max(lk, 0) * C::ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, kvbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, kvbytes);
+  auto issue = [&](int u) {
+    unsigned char* kbuf = ring[u % C::NS][0];
+    unsigned char* vbuf = ring[u % C::NS][1];
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i) {
+      const int blk = i * (C::NT / 64) + wave;
+      const int p = blk * 64 + lane;
+      const int row = p / C::CPR;
+      const int cc = p - row * C::CPR;
+      const uint32_t rb = (uint32_t)(u * C::UNIT + row) * C::ROW;
+      dma16(kr, rb + (uint32_t)((cc ^ kswz<D>(row)) * 16), kbuf + blk * 1024);
+      dma16(vr, rb + (uint32_t)(cc * 16), vbuf + blk * 1024);
+    }
+  };
+
+  // ---- Q^T operands: lane holds Q[p0 + l32][h][ks*16 + cg*8 .. +8]
+  bf16x8 qop[C::KS];
   {
-    const int nrows = max(0, min(64, lq - p0));
+    const int nrows = max(0, min(32, lq - p0));
     const __amdgpu_buffer_rsrc_t qr =
         make_rsrc((const __bf16*)a.q + ((size_t)(q0 + max(p0, 0)) * Hq) * D,
                   has_rows ? (uint32_t)(nrows * Hq * C::ROW) : 0u);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const uint32_t o = (uint32_t)(((nt * 32 + l32) * Hq + h) * C::ROW + (ks * 16 + cg * 8) * 2);
-        qop[nt][ks] = as_bf16x8(load16(qr, o));
-      }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const uint32_t o = (uint32_t)((l32 * Hq + h) * C::ROW + (ks * 16 + cg * 8) * 2);
+      qop[ks] = as_bf16x8(load16(qr, o));
+    }
   }
 
   // ---- online-softmax state (log2 units), started from the head's sink
-  const float sig = (a.sinks != nullptr && active) ? a.sinks[h] * kLog2e : kNegInf;
-  float m[2] = {sig, sig};
-  const float d_init = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;  // counted once per row
-  float dsum[2] = {d_init, d_init};
-  f32x16 o[C::DT][2];
+  const float sig = (a.sinks != nullptr && has_rows) ? a.sinks[h] * kLog2e : kNegInf;
+  float m = sig;
+  float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;  // counted once per row
+  f32x16 o[C::DT];
 #pragma unroll
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[t][nt][j] = 0.f;
-
-  const size_t head_base = ((size_t)g * a.total_kv + kv0) * D;
+    for (int j = 0; j < 16; ++j) o[t][j] = 0.f;
   const float sl2 = a.scale_log2;
+  const int pos = p0 + l32;
+  const int lim = a.causal ? min(lk - 1, pos + off) : lk - 1;
 
-  // ---- global -> register -> LDS staging of one K/V tile
-  u32x4 kreg[C::NLD], vreg[C::NLD];
-  auto gload = [&](int kb) {
-    const uint32_t bytes = (uint32_t)max(0, min(C::BC, lk - kb)) * C::ROW;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base + (size_t)kb * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base + (size_t)kb * D, bytes);
 #pragma unroll
-    for (int i = 0; i < C::NLD; ++i) {
-      const int id = tid + 256 * i;
-      kreg[i] = load16(kr, (uint32_t)id * 16);
-      vreg[i] = load16(vr, (uint32_t)id * 16);
-    }
-  };
-  auto lwrite = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::NLD; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / C::CPR;
-      const int cc = id - row * C::CPR;
-      *(u32x4*)(lds_k + row * C::ROW + ((cc ^ kswz<D>(row)) * 16)) = kreg[i];
-      *(u32x4*)(lds_v + id * 16) = vreg[i];
-    }
-  };
+  for (int u = 0; u < C::PD; ++u) issue(u);
 
-  if (ntiles > 0) {
-    gload(0);
-    lwrite();
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int kb = it * C::BC;
-    if (it + 1 < ntiles) gload(kb + C::BC);
-
-    if (has_rows && kb < kend_w) {
-      // ---- S^T[key][row] for two 32-key tiles x two 32-row tiles
-      f32x16 s[2][2];
+  for (int u = 0; u < n_wg; ++u) {
+    // unit u has landed once only the PD-1 units issued after it are pending
+    wait_vmcnt<(C::PD - 1) * 2 * C::NDMA>();
+    __syncthreads();
+    issue(u + C::PD);  // refills the slot of unit u-1, which every wavefront finished
+    if (u < n_w) {
+      const unsigned char* kbuf = ring[u % C::NS][0];
+      const unsigned char* vbuf = ring[u % C::NS][1];
+      const int kbase = u * C::UNIT;
+      // ---- S^T: element j of key tile kt is key kbase + kt*32 + 8*(j/4) + 4*cg + j%4
+      f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) s[kt][nt][j] = 0.f;
+        for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        const int cc = ks * 2 + cg;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           const int row = kt * 32 + l32;
-          const int cc = ks * 2 + cg;
-          const bf16x8 ka = as_bf16x8(*(const u32x4*)(lds_k + row * C::ROW + ((cc ^ kswz<D>(row)) * 16)));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) s[kt][nt] = mfma32(ka, qop[nt][ks], s[kt][nt]);
+          const bf16x8 ka =
+              as_bf16x8(*(const u32x4*)(kbuf + row * C::ROW + ((cc ^ kswz<D>(row)) * 16)));
+          s[kt] = mfma32(ka, qop[ks], s[kt]);
         }
       }
-
-      // ---- mask (only tiles that cross the causal diagonal or the sequence end).
-      // Accumulator element j of key tile kt is key kb + kt*32 + 8*(j/4) + 4*cg + j%4.
-      const bool need_mask = (kb + C::BC > lk) || (a.causal && kb + C::BC - 1 > p0 + off);
-      if (need_mask) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int pos = p0 + nt * 32 + l32;
-          const int lim = a.causal ? min(lk - 1, pos + off) : lk - 1;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int key = kb + kt * 32 + 8 * (j >> 2) + 4 * cg + (j & 3);
-              s[kt][nt][j] = (key <= lim) ? s[kt][nt][j] : kNegInf;
-            }
-        }
-      }
-
-      // ---- online softmax; P^T packed as the B operands of the four 16-key PV steps
-      bf16x8 pop[2][2][2];  // [kt][kk][nt]
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float mx = kNegInf;
+      // ---- mask only where the unit crosses the diagonal or the sequence end
+      if (kbase + C::UNIT > lk || (a.causal && kbase + C::UNIT - 1 > p0 + off)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][nt][j]);
-        mx = wave_xor_max(mx, 32);
-        const float mnew = fmaxf(m[nt], mx * sl2);
-        const bool dead = (mnew == kNegInf);
-        const float alpha = dead ? 1.0f : fast_exp2(m[nt] - mnew);
-        const float msub = dead ? 0.0f : mnew;
-        float ps = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          float p[16];
-#pragma unroll
           for (int j = 0; j < 16; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(s[kt][nt][j], sl2, -msub));
-            ps += p[j];
+            const int key = kbase + kt * 32 + 8 * (j >> 2) + 4 * cg + (j & 3);
+            s[kt][j] = (key <= lim) ? s[kt][j] : kNegInf;
           }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            u32x4 pk;
-            pk.x = pack_bf16x2(p[kk * 8 + 0], p[kk * 8 + 1]);
-            pk.y = pack_bf16x2(p[kk * 8 + 2], p[kk * 8 + 3]);
-            pk.z = pack_bf16x2(p[kk * 8 + 4], p[kk * 8 + 5]);
-            pk.w = pack_bf16x2(p[kk * 8 + 6], p[kk * 8 + 7]);
-            pop[kt][kk][nt] = as_bf16x8(pk);
-          }
-        }
-        dsum[nt] = __builtin_fmaf(dsum[nt], alpha, ps);
-        m[nt] = mnew;
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) o[t][nt] *= alpha;
       }
-
+      // ---- row max; the running max is raised only when it grows by more than 2^8
+      float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int j = 2; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[0][j]), s[0][j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[1][j]), s[1][j + 1]);
+      const float mxs = half_swap_max(mx) * sl2;
+      if (__any(mxs > m + 8.0f)) {
+        const float mnew = fmaxf(m, mxs);
+        const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+        dsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+        m = mnew;
+      }
+      const float msub = (m == kNegInf) ? 0.0f : m;
+      // ---- probabilities as bf16 B operands; row sums in fp32 before rounding
+      bf16x8 pk[2][2];  // [kt][kk]
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[kt][kk * 8 + i], sl2, -msub));
+          u32x4 w4;
+          w4.x = pack_bf16x2(p[0], p[1]);
+          w4.y = pack_bf16x2(p[2], p[3]);
+          w4.z = pack_bf16x2(p[4], p[5]);
+          w4.w = pack_bf16x2(p[6], p[7]);
+          dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          pk[kt][kk] = as_bf16x8(w4);
+        }
       // ---- O^T += V^T . P^T.  Slot i of 16-key step (kt, kk) for k-group cg is key
       // kt*32 + 16*kk + 8*(i/4) + 4*cg + i%4; the lane reads DT head dims
-      // [DT*l32, DT*l32 + DT) of those 8 rows and transposes them in registers, so
-      // d-tile t holds head dim DT*m + t in MFMA row m.
+      // [DT*l32, +DT) of those 8 rows and transposes them in registers, so d-tile t
+      // holds head dim DT*m + t in MFMA row m.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -235,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int row = kt * 32 + 16 * kk + 8 * (i >> 2) + 4 * cg + (i & 3);
-            const unsigned char* src = lds_v + row * C::ROW + l32 * C::DT * 2;
+            const unsigned char* src = vbuf + row * C::ROW + l32 * C::DT * 2;
             if constexpr (C::DT == 4) {
               const u32x2 t2 = *(const u32x2*)src;
               vw[i][0] = t2.x;
@@ -247,70 +231,60 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int t = 0; t < C::DT; ++t) {
             u32x4 va;
-            const int w = t >> 1;
+            const int w2 = t >> 1;
             if ((t & 1) == 0) {
-              va.x = lo_lo(vw[0][w], vw[1][w]);
-              va.y = lo_lo(vw[2][w], vw[3][w]);
-              va.z = lo_lo(vw[4][w], vw[5][w]);
-              va.w = lo_lo(vw[6][w], vw[7][w]);
+              va.x = lo_lo(vw[0][w2], vw[1][w2]);
+              va.y = lo_lo(vw[2][w2], vw[3][w2]);
+              va.z = lo_lo(vw[4][w2], vw[5][w2]);
+              va.w = lo_lo(vw[6][w2], vw[7][w2]);
             } else {
-              va.x = hi_hi(vw[0][w], vw[1][w]);
-              va.y = hi_hi(vw[2][w], vw[3][w]);
-              va.z = hi_hi(vw[4][w], vw[5][w]);
-              va.w = hi_hi(vw[6][w], vw[7][w]);
+              va.x = hi_hi(vw[0][w2], vw[1][w2]);
+              va.y = hi_hi(vw[2][w2], vw[3][w2]);
+              va.z = hi_hi(vw[4][w2], vw[5][w2]);
+              va.w = hi_hi(vw[6][w2], vw[7][w2]);
             }
-            const bf16x8 vop = as_bf16x8(va);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) o[t][nt] = mfma32(vop, pop[kt][kk][nt], o[t][nt]);
+            o[t] = mfma32(as_bf16x8(va), pk[kt][kk], o[t]);
           }
         }
     }
-
-    __syncthreads();
-    if (it + 1 < ntiles) lwrite();
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
-  if (!has_rows) return;
-  // ---- epilogue.  O^T element (t, j) of column tile nt is head dim
-  // DT*(8*(j/4) + 4*cg + j%4) + t of query position p0 + nt*32 + l32.
+  if (!has_rows || pos >= lq) return;
+  // ---- epilogue.  O^T element (t, j) is head dim DT*(8*(j/4) + 4*cg + j%4) + t of
+  // query position pos.
+  const float dr = half_swap_sum(dsum);
+  const float inv = dr > 0.f ? 1.0f / dr : 0.f;
+  const size_t orow = (size_t)(q0 + pos) * Hq + h;
+  __bf16* dst = (__bf16*)a.out + orow * D;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float dr = wave_xor_sum(dsum[nt], 32);
-    const int pos = p0 + nt * 32 + l32;
-    if (pos >= lq) continue;
-    const float inv = dr > 0.f ? 1.0f / dr : 0.f;
-    const size_t orow = (size_t)(q0 + pos) * Hq + h;
-    __bf16* dst = (__bf16*)a.out + orow * D;
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float vals[4 * C::DT];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float vals[4 * C::DT];
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int t = 0; t < C::DT; ++t) vals[jj * C::DT + t] = o[t][q4 * 4 + jj] * inv;
+    const int d0 = C::DT * (8 * q4 + 4 * cg);
 #pragma unroll
-        for (int t = 0; t < C::DT; ++t) vals[jj * C::DT + t] = o[t][nt][q4 * 4 + jj] * inv;
-      const int d0 = C::DT * (8 * q4 + 4 * cg);
-#pragma unroll
-      for (int e = 0; e < 4 * C::DT; e += 8) {
-        u32x4 w4;
-        w4.x = pack_bf16x2(vals[e + 0], vals[e + 1]);
-        w4.y = pack_bf16x2(vals[e + 2], vals[e + 3]);
-        w4.z = pack_bf16x2(vals[e + 4], vals[e + 5]);
-        w4.w = pack_bf16x2(vals[e + 6], vals[e + 7]);
-        *(u32x4*)(dst + d0 + e) = w4;
-      }
+    for (int e = 0; e < 4 * C::DT; e += 8) {
+      u32x4 w4;
+      w4.x = pack_bf16x2(vals[e + 0], vals[e + 1]);
+      w4.y = pack_bf16x2(vals[e + 2], vals[e + 3]);
+      w4.z = pack_bf16x2(vals[e + 4], vals[e + 5]);
+      w4.w = pack_bf16x2(vals[e + 6], vals[e + 7]);
+      *(u32x4*)(dst + d0 + e) = w4;
     }
-    if (cg == 0 && a.lse != nullptr)
-      a.lse[orow] = dr > 0.f ? (m[nt] + __builtin_log2f(dr)) * kLn2 : kNegInf;
   }
+  if (cg == 0 && a.lse != nullptr)
+    a.lse[orow] = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
   dim3 grid((unsigned)(num_kv_heads * a.n_hgroups), (unsigned)a.batch, (unsigned)a.n_qtiles);
   if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

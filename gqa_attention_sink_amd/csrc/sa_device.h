@@ -12,6 +12,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -23,8 +25,14 @@ constexpr int kBufferWord3 = 0x00020000;
 // A bounded view of `bytes` bytes at `base`: loads at offsets >= bytes return zero
 // instead of touching memory, which is how every tail (keys past a sequence's end,
 // queries past a tile) is handled without branches or faults.
+// Both arguments must be wave-uniform; they are pinned to scalar registers so the
+// descriptor never needs a per-lane loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* up = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
                                            kBufferWord3);
 }
 
@@ -68,8 +76,16 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// acc + lo16(x) + hi16(x) for a packed bf16 pair (sum in fp32).
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
+// max / sum over the two lanes l and l^32 (the two halves of the wavefront).
+__device__ __forceinline__ float half_swap_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+__device__ __forceinline__ float half_swap_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -81,11 +97,22 @@ __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
 }
 
 // Halves of two packed bf16 pairs: (lo16(x), lo16(y)) and (hi16(x), hi16(y)).
+// (v_perm_b32 selects bytes from {y:x}, x being bytes 0-3.)
 __device__ __forceinline__ uint32_t lo_lo(uint32_t x, uint32_t y) {
-  return (x & 0xffffu) | (y << 16);
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t hi_hi(uint32_t x, uint32_t y) {
-  return (x >> 16) | (y & 0xffff0000u);
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
+
+// Index of the calling wavefront inside its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Scheduling-group hints (instruction classes of sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedDsRead = 0x100;
 
 }  // namespace sa

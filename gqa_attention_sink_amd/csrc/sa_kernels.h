@@ -18,9 +18,9 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t group;      // query heads per KV head
   int32_t hg;         // query heads per workgroup (divides group, <= 4)
-  int32_t pw;         // 64-position blocks per workgroup (= 4 / hg)
+  int32_t pw;         // 32-position blocks per workgroup (= 8 / hg)
   int32_t n_hgroups;  // group / hg
-  int32_t n_qtiles;   // ceil(max_seqlen_q / (64 * pw))
+  int32_t n_qtiles;   // ceil(max_seqlen_q / (32 * pw))
   int32_t causal;
   float scale_log2;   // sm_scale * log2(e)
   void* out;

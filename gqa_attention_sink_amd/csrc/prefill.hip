@@ -48,6 +48,10 @@ __device__ __forceinline__ int kswz(int row) {
   else return (row >> 1) & 7;
 }
 
+// XOR swizzle of 16-byte chunks inside a V row: the 8 rows touched by one transposing
+// read land in distinct banks.
+__device__ __forceinline__ int vswz(int row) { return row & 7; }
+
 template <int D>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D>;
@@ -60,7 +64,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
   const int cg = lane >> 5;
   const int Hq = a.num_q_heads;
 
-  const int hgi = blockIdx.x;
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2); when the
+  // head-group axis is a multiple of 8, give each XCD a contiguous range of head groups
+  // so the K/V of a KV head stays in few L2s.
+  int hgi = blockIdx.x;
+  if ((gridDim.x & 7) == 0) hgi = (hgi & 7) * (int)(gridDim.x >> 3) + (hgi >> 3);
   const int g = hgi / a.n_hgroups;
   const int hgrp = hgi - g * a.n_hgroups;
   const int b = blockIdx.y;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
       const int cc = p - row * C::CPR;
       const uint32_t rb = (uint32_t)(u * C::UNIT + row) * C::ROW;
       dma16(kr, rb + (uint32_t)((cc ^ kswz<D>(row)) * 16), kbuf + blk * 1024);
-      dma16(vr, rb + (uint32_t)(cc * 16), vbuf + blk * 1024);
+      dma16(vr, rb + (uint32_t)((cc ^ vswz(row)) * 16), vbuf + blk * 1024);
     }
   };
 
@@ -134,6 +142,21 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
   const float sl2 = a.scale_log2;
   const int pos = p0 + l32;
   const int lim = a.causal ? min(lk - 1, pos + off) : lk - 1;
+
+  // Per-lane part of the transposing V reads: lane p of each 16-lane group supplies
+  // row 4*cg + p/4 (+ a multiple of 8, which leaves the swizzle unchanged) at head dims
+  // 32*t + 16*((lane/16)%2) + 4*(p%4).
+  uint32_t v_lane_off[C::DT];
+  {
+    const int p16 = lane & 15;
+    const int lrow = 4 * cg + (p16 >> 2);
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (p16 & 3);
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) {
+      const int d = 32 * t + dsub;
+      v_lane_off[t] = (uint32_t)(lrow * C::ROW + (((d >> 3) ^ vswz(lrow)) * 16) + (d & 7) * 2);
+    }
+  }
 
 #pragma unroll
   for (int u = 0; u < C::PD; ++u) issue(u);
@@ -208,73 +231,58 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
           pk[kt][kk] = as_bf16x8(w4);
         }
       // ---- O^T += V^T . P^T.  Slot i of 16-key step (kt, kk) for k-group cg is key
-      // kt*32 + 16*kk + 8*(i/4) + 4*cg + i%4; the lane reads DT head dims
-      // [DT*l32, +DT) of those 8 rows and transposes them in registers, so d-tile t
-      // holds head dim DT*m + t in MFMA row m.
+      // kt*32 + 16*kk + 8*(i/4) + 4*cg + i%4, read transposed from LDS: for half h of
+      // the slots, lane p of each 16-lane group supplies key row
+      // kt*32 + 16*kk + 8*h + 4*cg + p/4 at head dims 32*t + 16*((lane/16)%2) + 4*(p%4),
+      // so lane l receives V[slot keys][32*t + l%32] (d-tile t, MFMA row l%32).
+      uint32_t vaddr[C::DT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int t = 0; t < C::DT; ++t) vaddr[t] = lds_addr(vbuf) + v_lane_off[t];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        u32x2 vr2[2][C::DT][2];  // [kk][t][h]
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              vr2[kk][t][hh] = ds_read_tr16(vaddr[t], (kt * 32 + 16 * kk + 8 * hh) * C::ROW);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          uint32_t vw[8][C::DT / 2];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int row = kt * 32 + 16 * kk + 8 * (i >> 2) + 4 * cg + (i & 3);
-            const unsigned char* src = vbuf + row * C::ROW + l32 * C::DT * 2;
-            if constexpr (C::DT == 4) {
-              const u32x2 t2 = *(const u32x2*)src;
-              vw[i][0] = t2.x;
-              vw[i][1] = t2.y;
-            } else {
-              vw[i][0] = *(const uint32_t*)src;
-            }
+          if constexpr (C::DT == 4) {
+            lds_wait(vr2[kk][0][0], vr2[kk][0][1], vr2[kk][1][0], vr2[kk][1][1]);
+            lds_wait(vr2[kk][2][0], vr2[kk][2][1], vr2[kk][3][0], vr2[kk][3][1]);
+          } else {
+            lds_wait(vr2[kk][0][0], vr2[kk][0][1], vr2[kk][1][0], vr2[kk][1][1]);
           }
 #pragma unroll
           for (int t = 0; t < C::DT; ++t) {
-            u32x4 va;
-            const int w2 = t >> 1;
-            if ((t & 1) == 0) {
-              va.x = lo_lo(vw[0][w2], vw[1][w2]);
-              va.y = lo_lo(vw[2][w2], vw[3][w2]);
-              va.z = lo_lo(vw[4][w2], vw[5][w2]);
-              va.w = lo_lo(vw[6][w2], vw[7][w2]);
-            } else {
-              va.x = hi_hi(vw[0][w2], vw[1][w2]);
-              va.y = hi_hi(vw[2][w2], vw[3][w2]);
-              va.z = hi_hi(vw[4][w2], vw[5][w2]);
-              va.w = hi_hi(vw[6][w2], vw[7][w2]);
-            }
+            const u32x4 va = {vr2[kk][t][0].x, vr2[kk][t][0].y, vr2[kk][t][1].x, vr2[kk][t][1].y};
             o[t] = mfma32(as_bf16x8(va), pk[kt][kk], o[t]);
           }
         }
+      }
     }
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
   if (!has_rows || pos >= lq) return;
-  // ---- epilogue.  O^T element (t, j) is head dim DT*(8*(j/4) + 4*cg + j%4) + t of
-  // query position pos.
+  // ---- epilogue.  O^T element (t, j) is head dim 32*t + 8*(j/4) + 4*cg + j%4 of
+  // query position pos: four runs of 4 consecutive head dims per d-tile.
   const float dr = half_swap_sum(dsum);
   const float inv = dr > 0.f ? 1.0f / dr : 0.f;
   const size_t orow = (size_t)(q0 + pos) * Hq + h;
   __bf16* dst = (__bf16*)a.out + orow * D;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    float vals[4 * C::DT];
+  for (int t = 0; t < C::DT; ++t)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int t = 0; t < C::DT; ++t) vals[jj * C::DT + t] = o[t][q4 * 4 + jj] * inv;
-    const int d0 = C::DT * (8 * q4 + 4 * cg);
-#pragma unroll
-    for (int e = 0; e < 4 * C::DT; e += 8) {
-      u32x4 w4;
-      w4.x = pack_bf16x2(vals[e + 0], vals[e + 1]);
-      w4.y = pack_bf16x2(vals[e + 2], vals[e + 3]);
-      w4.z = pack_bf16x2(vals[e + 4], vals[e + 5]);
-      w4.w = pack_bf16x2(vals[e + 6], vals[e + 7]);
-      *(u32x4*)(dst + d0 + e) = w4;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 w2;
+      w2.x = pack_bf16x2(o[t][q4 * 4 + 0] * inv, o[t][q4 * 4 + 1] * inv);
+      w2.y = pack_bf16x2(o[t][q4 * 4 + 2] * inv, o[t][q4 * 4 + 3] * inv);
+      *(u32x2*)(dst + 32 * t + 8 * q4 + 4 * cg) = w2;
     }
-  }
   if (cg == 0 && a.lse != nullptr)
     a.lse[orow] = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
 }

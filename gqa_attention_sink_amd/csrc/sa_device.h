@@ -105,6 +105,28 @@ __device__ __forceinline__ uint32_t hi_hi(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of an 8-byte piece (4 elements); lane i receives
+// element i%4 of the pieces of lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.  With lane j
+// pointing at row j/4, columns 4*(j%4)..+3 of a 4-row x 16-column block, lane i gets
+// column i of the 4 rows.  Written as inline assembly so that no wait for pending
+// buffer->LDS copies is attached to it: the caller orders it after its own waits and
+// barrier, and must call lds_wait() before using the result.
+// `off` must fold to a constant in [0, 65535] (the instruction's immediate offset).
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr, const int off) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(off) : "memory");
+  return r;
+}
+// Wait for all outstanding LDS reads; ties the given registers to the wait.
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : : "memory");
+}
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Index of the calling wavefront inside its workgroup, as a wave-uniform value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

@@ -28,7 +28,7 @@ inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 inline int planned_slots(int32_t max_kv_len, int32_t num_splits) {
   if (num_splits > 0) return num_splits;
-  int n = (int)((max_kv_len + 511) / 512);
+  int n = (int)((max_kv_len + 255) / 256);
   return n < 4 ? 4 : (n > 16 ? 16 : n);
 }
 

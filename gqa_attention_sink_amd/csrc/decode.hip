@@ -22,10 +22,10 @@
 namespace sa {
 
 // Split planner: chunk count of a sequence with lk keys and the chunk's key range.
-// num_splits > 0 forces that many chunks; 0 picks clamp(ceil(lk/512), 4, 16).  Every
+// num_splits > 0 forces that many chunks; 0 picks clamp(ceil(lk/256), 4, 16).  Every
 // chunk spans the same 32-key-aligned length, so trailing chunks may be empty.
 __device__ __forceinline__ int plan_chunks(int lk, int num_splits) {
-  return num_splits > 0 ? num_splits : min(16, max(4, (lk + 511) >> 9));
+  return num_splits > 0 ? num_splits : min(16, max(4, (lk + 255) >> 8));
 }
 __device__ __forceinline__ int chunk_len(int lk, int n) {
   int cl = lk > 0 ? (lk + n - 1) / n : 0;

@@ -87,7 +87,7 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
  *             sits at position Lk - q_len + t; with causal=1 it sees keys <= that
  *             position (causal within the draft).
  *  max_kv_len host upper bound of kv_indptr[b+1]-kv_indptr[b].
- *  num_splits 0 = planner: clamp(ceil(Lk/512), 4, 16) chunks for each sequence;
+ *  num_splits 0 = planner: clamp(ceil(Lk/256), 4, 16) chunks for each sequence;
  *             k in 1..64 = exactly k chunks per sequence.  A chunk holds
  *             ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
  *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,

@@ -180,14 +180,14 @@ def plan_chunks(lk: int, num_splits: int, tile: int = 32) -> list[int]:
 
     The pages split attention along the KV length into blocks ("Sink attention") and
     parallelise over heads and KV length, but fix no block size.  Reading used here:
-    n = num_splits if num_splits > 0, else clamp(ceil(lk / 512), 4, 16); every chunk
+    n = num_splits if num_splits > 0, else clamp(ceil(lk / 256), 4, 16); every chunk
     has the same length, ceil(lk / n) rounded up to a multiple of ``tile``, so trailing
     chunks may be empty.
     """
     if num_splits > 0:
         n = num_splits
     else:
-        n = min(16, max(4, -(-lk // 512)))
+        n = min(16, max(4, -(-lk // 256)))
     cl = -(-lk // n) if lk > 0 else 0
     cl = -(-cl // tile) * tile
     return [min(lk, c * cl) for c in range(n)] + [lk]

@@ -115,7 +115,7 @@ def test_merge_validation(lib):
 def test_planner_slots(lib):
     ns = lib.sink_attn_decode_num_slots
     assert ns(8192, 0) == 16 and ns(1024, 0) == 4 and ns(100, 0) == 4 and ns(0, 0) == 4
-    assert ns(4097, 0) == 9 and ns(100000, 0) == 16
+    assert ns(2049, 0) == 9 and ns(4097, 0) == 16 and ns(100000, 0) == 16
     assert ns(32768, 32) == 32 and ns(10, 1) == 1
     assert ns(10, 65) == 0 and ns(-1, 0) == 0
 

@@ -194,13 +194,13 @@ def test_merge_handles_empty_chunks():
 
 
 def test_plan_chunks_rule():
-    for lk in (1, 31, 32, 511, 512, 1024, 4097, 8192):
+    for lk in (1, 31, 32, 255, 256, 511, 512, 1024, 4097, 8192):
         b = plan_chunks(lk, 0)
         n = len(b) - 1
-        assert n == min(16, max(4, -(-lk // 512)))
+        assert n == min(16, max(4, -(-lk // 256)))
         assert b[0] == 0 and b[-1] == lk and all(x <= y for x, y in zip(b, b[1:]))
         assert all(x % 32 == 0 or x == lk for x in b)
-    assert len(plan_chunks(1024, 0)) - 1 == 4 and len(plan_chunks(8192, 0)) - 1 == 16
+    assert len(plan_chunks(1024, 0)) - 1 == 4 and len(plan_chunks(4096, 0)) - 1 == 16
     assert plan_chunks(32768, 32) == list(range(0, 32768, 1024)) + [32768]
 
 

@@ -101,8 +101,7 @@ def _traffic_for(kernel, workload):
 
 
 def bench_decode(sa, w, steps, warmup, flush):
-    ws = torch.empty(sa.decode_workspace_bytes(w.batch, w.q_len, w.hq, w.d, w.max_kv,
-                                               w.num_splits), dtype=torch.uint8, device="cuda")
+    ws = sa.decode_workspace(w.batch, w.q_len, w.hq, w.d, w.max_kv, w.num_splits)
     out = torch.empty_like(w.q)
     lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
     s = sa.decode_num_slots(w.max_kv, w.num_splits)

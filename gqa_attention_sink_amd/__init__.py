@@ -9,6 +9,7 @@ from .sink_attn import (  # noqa: F401
     decode,
     decode_num_slots,
     decode_partial,
+    decode_workspace,
     decode_workspace_bytes,
     load,
     merge,

@@ -280,41 +280,52 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One wavefront per row: weights from the partial lse, then the weighted sum of the
-// partial outputs.  Slots with lse = -inf are skipped (their output is not read).
+// Merge: D/4 lanes per row, each owning four consecutive head dims, so a row's
+// partial outputs are read as whole 16-byte vectors and a wavefront covers 256/D rows.
+// Slots are taken four at a time: the four loads are issued together, and a group
+// whose weights are all zero is skipped.  A slot with lse = -inf has weight 0 and its
+// partial output (possibly never written) is selected away, never multiplied.
+constexpr int kMergeThreads = 128;
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_lse,
-                                                    int64_t rows, int S, __bf16* out,
-                                                    float* lse) {
-  constexpr int E = D / 64;  // head dims per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_lse,
+                                                              int64_t rows, int S, __bf16* out,
+                                                              float* lse) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = kMergeThreads / LPR;
+  const int q = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   if (row >= rows) return;
   const float* pl = part_lse + row * S;
+  const f32x4* po = (const f32x4*)(part_o + row * S * D) + q;
   float mx = kNegInf;
-  for (int c = lane; c < S; c += 64) mx = fmaxf(mx, pl[c]);
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) mx = wave_xor_max(mx, msk);
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int c = 0; c < S; ++c) mx = fmaxf(mx, pl[c]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != kNegInf) {
-    const float* po = part_o + row * S * D + lane * E;
-    for (int c = 0; c < S; ++c) {
-      const float w = __expf(pl[c] - mx);
-      if (w == 0.f) continue;
-      wsum += w;
+    for (int c = 0; c < S; c += 4) {
+      float w[4];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w, po[(size_t)c * D + e], acc[e]);
+      for (int u = 0; u < 4; ++u) w[u] = (c + u < S) ? __expf(pl[c + u] - mx) : 0.f;
+      if ((w[0] + w[1]) + (w[2] + w[3]) == 0.f) continue;
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = po[(size_t)min(c + u, S - 1) * (D / 4)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wsum += w[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[e] = (w[u] != 0.f) ? __builtin_fmaf(w[u], x[u][e], acc[e]) : acc[e];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  __bf16* dst = out + row * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = (__bf16)(acc[e] * inv);
-  if (lane == 0 && lse != nullptr) lse[row] = wsum > 0.f ? mx + __logf(wsum) : kNegInf;
+  u32x2 pk;
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)(out + row * D + 4 * q) = pk;
+  if (q == 0 && lse != nullptr) lse[row] = wsum > 0.f ? mx + __logf(wsum) : kNegInf;
 }
 
 template <int D, bool DIRECT>
@@ -340,13 +351,12 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int
 
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows, int num_slots,
                         int head_dim, void* out, float* lse, hipStream_t stream) {
-  dim3 grid((unsigned)((rows + 3) / 4));
   if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, part_o, part_lse, rows,
-                       num_slots, (__bf16*)out, lse);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)((rows + 7) / 8)), dim3(kMergeThreads),
+                       0, stream, part_o, part_lse, rows, num_slots, (__bf16*)out, lse);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, part_o, part_lse, rows,
-                       num_slots, (__bf16*)out, lse);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)((rows + 3) / 4)), dim3(kMergeThreads),
+                       0, stream, part_o, part_lse, rows, num_slots, (__bf16*)out, lse);
   return hipGetLastError();
 }
 

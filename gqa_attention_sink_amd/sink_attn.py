@@ -158,6 +158,14 @@ def decode_workspace_bytes(batch: int, q_len: int, num_q_heads: int, head_dim: i
                                                        int(max_kv_len), int(num_splits)))
 
 
+def decode_workspace(batch: int, q_len: int, num_q_heads: int, head_dim: int,
+                     max_kv_len: int, num_splits: int = 0, device="cuda"):
+    """A uint8 workspace for decode() of these sizes (contents need no initialisation);
+    stream-ordered calls of any sizes it fits may share it."""
+    nbytes = decode_workspace_bytes(batch, q_len, num_q_heads, head_dim, max_kv_len, num_splits)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
 def _decode_common(q, k, v, kv_indptr):
     _dev_tensor(q, torch.bfloat16, "q", 4)
     _dev_tensor(k, torch.bfloat16, "k", 3)
@@ -178,14 +186,14 @@ def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float]
     q [B, q_len, Hq, D] bf16 (q_len 1..4); k, v [Hkv, total_kv, D] bf16 (HND);
     kv_indptr int32 [B+1] (the KV already holds the q_len new tokens); max_kv_len a
     host int.  workspace: a uint8 GPU tensor of at least decode_workspace_bytes(...)
-    bytes (allocated here if None).  Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq])."""
+    bytes (decode_workspace() makes one; allocated here if None).  Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq])."""
     lib = load()
     b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
     sinks = _sinks_arg(sinks, hq, q.device)
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     nbytes = decode_workspace_bytes(b, ql, hq, d, max_kv_len, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(b, ql, hq, d, max_kv_len, num_splits, q.device)
     else:
         _dev_tensor(workspace, torch.uint8, "workspace")
     if out is None:

@@ -269,6 +269,44 @@ def test_decode_split_invariance(sa):
         _compare(out, lse, ro, rl, f"num_splits={ns}")
 
 
+def test_decode_workspace_reuse(sa):
+    """One workspace serves stream-ordered calls of different sizes in a row; every
+    result still matches the oracle."""
+    big = wl.make_decode([3000, 17, 900, 4096], 2, 64, 8, 64, ("normal", 0, 2), 0.125, True,
+                         0, seed=410, device="cuda")
+    small = wl.make_decode([33, 700, 5], 1, 8, 1, 128, ("normal", 0, 2), 1 / math.sqrt(128),
+                           True, 7, seed=411, device="cuda")
+    nb = max(sa.decode_workspace_bytes(w.batch, w.q_len, w.hq, w.d, w.max_kv, w.num_splits)
+             for w in (big, small))
+    ws = torch.full((nb,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage contents
+    refs = {id(w): _oracle_decode(w) for w in (big, small)}
+    for i, w in enumerate((big, small, big, small, small)):
+        _say(f"workspace reuse call {i}: batch={w.batch} d={w.d}")
+        out, lse = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                             w.causal, w.num_splits, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = refs[id(w)]
+        _compare(out, lse, ro, rl, f"reuse call {i}")
+
+
+def test_decode_large_batch_sampled(sa):
+    """2100 short sequences (a grid with 2100 x 8 x 4 workgroups); 23 whole sequences
+    are checked against the oracle."""
+    g = torch.Generator().manual_seed(420)
+    lens = (torch.randint(1, 300, (2100,), generator=g)).tolist()
+    w = wl.make_decode(lens, 1, 16, 8, 64, ("normal", 0, 2), 0.125, True, 0, seed=421,
+                       device="cuda")
+    _say("large batch 2100")
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ind = w.cu_seqlens_kv.cpu().tolist()
+    for b in list(range(0, 2100, 97)) + [2099]:
+        ks = slice(ind[b], ind[b + 1])
+        ro, rl = oracle.sink_attention_decode(w.q[b:b + 1], w.k[:, ks], w.v[:, ks], w.sinks,
+                                              [0, ind[b + 1] - ind[b]], w.scale, w.causal)
+        _compare(out[b:b + 1], lse[b:b + 1], ro, rl, f"large batch b={b}")
+
+
 # ------------------------------------------------------------------ bit-exact properties
 def test_prefill_masked_positions_bitwise(sa):
     w = wl.make_prefill([70, 130], [70, 130], 8, 2, 64, ("normal", 0, 2), 0.125, True,

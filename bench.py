@@ -101,10 +101,10 @@ def _traffic_for(kernel, workload):
 
 
 def bench_decode(sa, w, steps, warmup, flush):
-    ws = sa.decode_workspace(w.batch, w.q_len, w.hq, w.d, w.max_kv, w.num_splits)
+    ws = sa.decode_workspace(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
     out = torch.empty_like(w.q)
     lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
-    s = sa.decode_num_slots(w.max_kv, w.num_splits)
+    s = sa.decode_num_slots(w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
     rows = w.batch * w.q_len * w.hq
     po = torch.empty((rows, s, w.d), dtype=torch.float32, device="cuda")
     pl = torch.empty((rows, s), dtype=torch.float32, device="cuda")

@@ -7,6 +7,7 @@ from .sink_attn import (  # noqa: F401
     LIB_PATH,
     SinkAttnError,
     decode,
+    decode_chunks_per_slot,
     decode_num_slots,
     decode_partial,
     decode_workspace,

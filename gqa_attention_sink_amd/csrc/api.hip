@@ -26,10 +26,23 @@ inline bool dim_ok(int d) { return d == 64 || d == 128; }
 
 inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-inline int planned_slots(int32_t max_kv_len, int32_t num_splits) {
+// Largest chunk count of the decode plan (the device applies the same rule per
+// sequence): num_splits > 0 forces it; otherwise ceil(Lk/256) rounded up to a multiple of
+// cw (chunks per workgroup) and clamped to [4, 16].
+inline int planned_chunks(int32_t max_kv_len, int32_t num_splits, int cw) {
   if (num_splits > 0) return num_splits;
   int n = (int)((max_kv_len + 255) / 256);
+  n = (n + cw - 1) / cw * cw;
   return n < 4 ? 4 : (n > 16 ? 16 : n);
+}
+
+// Partial slots per row: one per group of cw consecutive chunks.
+inline int planned_slots(int32_t max_kv_len, int32_t num_splits, int cw) {
+  return (planned_chunks(max_kv_len, num_splits, cw) + cw - 1) / cw;
+}
+
+inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
+  return sa::decode_chunk_waves(q_len * (hq / hkv), d);
 }
 
 // Query heads per prefill workgroup: the largest divisor of the GQA group size <= 4.
@@ -60,8 +73,8 @@ int check_decode_args(const void* q, const void* k, const void* v, const int32_t
 
 sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const float* sinks,
                            const int32_t* kv_indptr, int32_t q_len, int64_t total_kv,
-                           int32_t max_kv_len, int32_t hq, int32_t hkv, float sm_scale,
-                           int32_t causal, int32_t num_splits) {
+                           int32_t max_kv_len, int32_t hq, int32_t hkv, int32_t d,
+                           float sm_scale, int32_t causal, int32_t num_splits) {
   sa::DecodeArgs a{};
   a.q = q;
   a.k = k;
@@ -76,7 +89,8 @@ sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const fl
   const int w = sa::decode_waves(rows);
   a.row_groups = (rows + 16 * w - 1) / (16 * w);
   a.num_splits = num_splits;
-  a.num_slots = planned_slots(max_kv_len, num_splits);
+  a.chunk_waves = chunk_waves(q_len, hq, hkv, d);
+  a.num_slots = planned_slots(max_kv_len, num_splits, a.chunk_waves);
   a.causal = causal;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return a;
@@ -148,19 +162,33 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
   }
 }
 
-int32_t sink_attn_decode_num_slots(int32_t max_kv_len, int32_t num_splits) {
-  if (max_kv_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return 0;
-  return planned_slots(max_kv_len, num_splits);
+static bool slot_args_ok(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
+  return q_len >= 1 && q_len <= 4 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && dim_ok(d);
+}
+
+int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim) {
+  if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim)) return 0;
+  return chunk_waves(q_len, num_q_heads, num_kv_heads, head_dim);
+}
+
+int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_kv_len, int32_t num_splits) {
+  if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || max_kv_len < 0 ||
+      num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  return planned_slots(max_kv_len, num_splits,
+                       chunk_waves(q_len, num_q_heads, num_kv_heads, head_dim));
 }
 
 size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
-                                        int32_t head_dim, int32_t max_kv_len,
-                                        int32_t num_splits) {
-  if (batch < 1 || q_len < 1 || q_len > 4 || num_q_heads < 1 || !dim_ok(head_dim) ||
-      max_kv_len < 0 || num_splits < 0 || num_splits > kMaxSplits)
-    return 0;
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_kv_len, int32_t num_splits) {
+  if (batch < 1) return 0;
+  const int64_t S = sink_attn_decode_num_slots(q_len, num_q_heads, num_kv_heads, head_dim,
+                                               max_kv_len, num_splits);
+  if (S == 0) return 0;
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
-  const int64_t S = planned_slots(max_kv_len, num_splits);
   int64_t bytes = rows * S * head_dim * 4;   // partial outputs
   bytes = (bytes + 255) & ~(int64_t)255;
   bytes += rows * S * 4;                     // partial lse
@@ -180,7 +208,8 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
     if (!part_o || !part_lse) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
     sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
-                                   num_q_heads, num_kv_heads, sm_scale, causal, num_splits);
+                                   num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
+                                   num_splits);
     a.part_o = part_o;
     a.part_lse = part_lse;
     hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, (hipStream_t)stream);
@@ -204,7 +233,8 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
     if (!out) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
     sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
-                                   num_q_heads, num_kv_heads, sm_scale, causal, num_splits);
+                                   num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
+                                   num_splits);
     hipStream_t st = (hipStream_t)stream;
     if (a.num_slots == 1) {  // one chunk per sequence: the split kernel writes the result
       a.out = out;
@@ -213,8 +243,8 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
       if (e != hipSuccess) return hip_fail(e);
       return SINK_ATTN_OK;
     }
-    const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, head_dim,
-                                                         max_kv_len, num_splits);
+    const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
+                                                         head_dim, max_kv_len, num_splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
       return SINK_ATTN_ERR_WORKSPACE;
     const int64_t rows = (int64_t)batch * q_len * num_q_heads;

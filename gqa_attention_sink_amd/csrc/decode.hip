@@ -22,10 +22,21 @@
 namespace sa {
 
 // Split planner: chunk count of a sequence with lk keys and the chunk's key range.
-// num_splits > 0 forces that many chunks; 0 picks clamp(ceil(lk/256), 4, 16).  Every
-// chunk spans the same 32-key-aligned length, so trailing chunks may be empty.
-__device__ __forceinline__ int plan_chunks(int lk, int num_splits) {
-  return num_splits > 0 ? num_splits : min(16, max(4, (lk + 255) >> 8));
+// num_splits > 0 forces that many chunks; 0 picks ceil(lk/256) rounded up to a multiple
+// of cw (the chunks one workgroup takes together) and clamped to [4, 16].  Every chunk
+// spans the same 32-key-aligned length, so trailing chunks may be empty.
+__device__ __forceinline__ int plan_chunks(int lk, int num_splits, int cw) {
+  if (num_splits > 0) return num_splits;
+  const int n = (((lk + 255) >> 8) + cw - 1) / cw * cw;
+  return min(16, max(4, n));
+}
+// Sequence b's token range, clamped to the token axis so that no copy can leave K or V
+// even when the index array is malformed.
+__device__ __forceinline__ int seq_begin(const DecodeArgs& a, int b) {
+  return (int)min<int64_t>(max(a.kv_indptr[b], 0), a.total_kv);
+}
+__device__ __forceinline__ int seq_end(const DecodeArgs& a, int b) {
+  return (int)min<int64_t>(max(a.kv_indptr[b + 1], seq_begin(a, b)), a.total_kv);
 }
 __device__ __forceinline__ int chunk_len(int lk, int n) {
   int cl = lk > 0 ? (lk + n - 1) / n : 0;
@@ -78,9 +89,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   const int Hq = a.num_q_heads;
   const int M = a.q_len * G;
 
-  const int kv0 = a.kv_indptr[b];
-  const int lk = a.kv_indptr[b + 1] - kv0;
-  const int n = plan_chunks(lk, a.num_splits);
+  const int kv0 = seq_begin(a, b);
+  const int lk = seq_end(a, b) - kv0;
+  const int n = plan_chunks(lk, a.num_splits, 1);
   const int cl = chunk_len(lk, n);
   const int S = a.num_slots;
 
@@ -280,6 +291,260 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// Chunk-wave decode kernel, for at most 16 query rows per KV head (q_len * G <= 16,
+// e.g. single-token decode with G = 8).  Workgroup = CW wavefronts = one (sequence,
+// KV head) and CW consecutive chunks of its plan, c = CW * blockIdx.x + w; each
+// wavefront streams its own chunk through its own NST-stage LDS ring (asynchronous
+// buffer->LDS copies, no barriers) exactly like a one-wavefront split kernel, and the
+// CW online-softmax states are then combined in LDS ("Sink attention": blocks along the
+// key axis merge by their log-sum-exp; the sink sits in chunk 0).  One partial (or,
+// with a single slot, the final output) leaves the workgroup instead of CW of them,
+// which cuts the partial traffic written during the KV stream and read by the merge.
+template <int D, int CW, bool DIRECT>
+__global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int DPL = D / 16;
+  constexpr int ROW = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int STEP = 32;
+  constexpr int NST = 4;                  // per-wavefront ring depth
+  constexpr int SB = STEP * ROW;
+  constexpr int NDMA = SB / (64 * 16);    // copies per lane per tensor per stage
+  static_assert(CW * NST * 2 * SB <= 160 * 1024, "LDS");
+  static_assert(CW * 16 * (D + 2) * 4 <= CW * NST * 2 * SB, "combine scratch fits the rings");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[CW][NST][2][SB];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int l16 = lane & 15;
+  const int cg = lane >> 4;
+  const int slot = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int M = a.q_len * G;
+  const int S = a.num_slots;
+
+  const int kv0 = seq_begin(a, b);
+  const int lk = seq_end(a, b) - kv0;
+  const int n = plan_chunks(lk, a.num_splits, CW);
+  const int cl = chunk_len(lk, n);
+
+  // The lane's query row R = l16 -> (draft token t, query head h).
+  const int row_t = l16 / G;
+  const int row_h = g * G + (l16 - row_t * G);
+  const bool row_ok = l16 < M;
+  const int64_t qrow = ((int64_t)b * a.q_len + row_t) * Hq + row_h;
+
+  if (slot * CW >= n) {  // unused slot: no mass
+    if (!DIRECT && w == 0 && cg == 0 && row_ok) a.part_lse[qrow * S + slot] = kNegInf;
+    return;
+  }
+  const int c = slot * CW + w;
+  const int kb = min(lk, c * cl);
+  const int ke = (c < n) ? min(lk, kb + cl) : kb;
+  const int nsteps = (ke - kb + STEP - 1) / STEP;
+
+  const size_t head_base = ((size_t)g * a.total_kv + kv0 + kb) * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, (uint32_t)(ke - kb) * ROW);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, (uint32_t)(ke - kb) * ROW);
+  unsigned char (*my)[2][SB] = ring[w];
+  auto issue = [&](int st) {
+    unsigned char* kbuf = my[st % NST][0];
+    unsigned char* vbuf = my[st % NST][1];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int p = i * 64 + lane;            // 16-byte chunk index inside the stage
+      const int row = p / CPR;
+      const int cc = p - row * CPR;
+      const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
+      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+    }
+  };
+
+  const uint32_t qbytes = (uint32_t)(a.q_len * Hq * ROW);
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc((const __bf16*)a.q + (size_t)b * a.q_len * Hq * D, qbytes);
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)((row_t * Hq + row_h) * ROW + (ks * 32 + cg * 8) * 2);
+    qop[ks] = as_bf16x8(load16(qr, row_ok ? off : qbytes));
+  }
+  float sig = kNegInf;
+  if (c == 0 && a.sinks != nullptr && row_ok) sig = a.sinks[row_h] * kLog2e;
+  float m = sig;
+  float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;
+  f32x4 o[DPL];
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const float sl2 = a.scale_log2;
+  const int causal_first_masked = a.causal ? (lk - a.q_len + 1) : 0x7fffffff;
+  const int lim = min(ke - 1, a.causal ? lk - a.q_len + row_t : 0x7fffffff);
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue(st);
+
+  for (int st = 0; st < nsteps; ++st) {
+    // stage st has landed once only the NST-2 stages issued after it are pending; the
+    // ring is this wavefront's own, and its reads of slot (st-1) have completed
+    wait_vmcnt<(NST - 2) * 2 * NDMA>();
+    issue(st + NST - 1);
+
+    const unsigned char* kbuf = my[st % NST][0];
+    const unsigned char* vbuf = my[st % NST][1];
+    const int kbase = kb + st * STEP;
+
+    f32x4 s2[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int row = kt * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *(const u32x4*)(kbuf + row * ROW + (((ks * 4 + cg) ^ dswz<D>(row)) * 16));
+        acc = mfma16(as_bf16x8(kv), qop[ks], acc);
+      }
+      s2[kt] = acc;
+    }
+    if (kbase + STEP > ke || kbase + STEP > causal_first_masked) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kbase + kt * 16 + 4 * cg + j;
+          s2[kt][j] = (key <= lim) ? s2[kt][j] : kNegInf;
+        }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                     fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float mxs = mx * sl2;
+    if (__any(mxs > m + 8.0f)) {
+      const float mnew = fmaxf(m, mxs);
+      const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+      dsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) o[t] *= alpha;
+      m = mnew;
+    }
+    const float msub = (m == kNegInf) ? 0.0f : m;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(__builtin_fmaf(s2[0][j], sl2, -msub));
+      p[4 + j] = fast_exp2(__builtin_fmaf(s2[1][j], sl2, -msub));
+    }
+    dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    u32x4 pk;
+    pk.x = pack_bf16x2(p[0], p[1]);
+    pk.y = pack_bf16x2(p[2], p[3]);
+    pk.z = pack_bf16x2(p[4], p[5]);
+    pk.w = pack_bf16x2(p[6], p[7]);
+    const bf16x8 pop = as_bf16x8(pk);
+
+    uint32_t vw[8][DPL / 2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned char* src = vbuf + slot_key(cg, i) * ROW + l16 * DPL * 2;
+      if constexpr (DPL == 8) {
+        const u32x4 t4 = *(const u32x4*)src;
+        vw[i][0] = t4.x; vw[i][1] = t4.y; vw[i][2] = t4.z; vw[i][3] = t4.w;
+      } else {
+        const u32x2 t2 = *(const u32x2*)src;
+        vw[i][0] = t2.x; vw[i][1] = t2.y;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) {
+      u32x4 va;
+      const int wd = t >> 1;
+      if ((t & 1) == 0) {
+        va.x = lo_lo(vw[0][wd], vw[1][wd]);
+        va.y = lo_lo(vw[2][wd], vw[3][wd]);
+        va.z = lo_lo(vw[4][wd], vw[5][wd]);
+        va.w = lo_lo(vw[6][wd], vw[7][wd]);
+      } else {
+        va.x = hi_hi(vw[0][wd], vw[1][wd]);
+        va.y = hi_hi(vw[2][wd], vw[3][wd]);
+        va.z = hi_hi(vw[4][wd], vw[5][wd]);
+        va.w = hi_hi(vw[6][wd], vw[7][wd]);
+      }
+      o[t] = mfma16(as_bf16x8(va), pop, o[t]);
+    }
+  }
+
+  // ---- combine the CW chunk states.  Wavefront w leaves, per row, its max (log2
+  // units), its sum and its unnormalised output (head dim DPL*(4*cg + j) + t of O^T
+  // element (t, j)) in LDS, over its own ring.
+  wait_vmcnt<0>();
+  __syncthreads();
+  float dr = wave_xor_sum(dsum, 16);
+  dr = wave_xor_sum(dr, 32);
+  float* red = (float*)&ring[0][0][0][0];          // [CW][16][D] outputs, then m, d
+  float* red_m = red + CW * 16 * D;                // [CW][16]
+  float* red_d = red_m + CW * 16;                  // [CW][16]
+  {
+    float* dst = red + (w * 16 + l16) * D + 4 * cg * DPL;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < DPL; t += 4)
+        *(f32x4*)(dst + j * DPL + t) = f32x4{o[t][j], o[t + 1][j], o[t + 2][j], o[t + 3][j]};
+    if (cg == 0) {
+      red_m[w * 16 + l16] = m;
+      red_d[w * 16 + l16] = dr;
+    }
+  }
+  __syncthreads();
+  // Wavefront w writes rows [16/CW * w, +16/CW); LPR lanes per row, four dims each.
+  constexpr int LPR = D / 4;
+  constexpr int RPP = 64 / LPR;                    // rows per pass
+  constexpr int RPW = 16 / CW;                     // rows per wavefront
+#pragma unroll
+  for (int r0 = 0; r0 < RPW; r0 += RPP) {
+    const int r = w * RPW + r0 + lane / LPR;
+    const int q4 = lane % LPR;
+    if (r0 + lane / LPR >= RPW || r >= M) continue;
+    float mstar = kNegInf;
+#pragma unroll
+    for (int x = 0; x < CW; ++x) mstar = fmaxf(mstar, red_m[x * 16 + r]);
+    const float msub = (mstar == kNegInf) ? 0.0f : mstar;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll
+    for (int x = 0; x < CW; ++x) {
+      const float dx = red_d[x * 16 + r];
+      const float sc = (dx > 0.f) ? fast_exp2(red_m[x * 16 + r] - msub) : 0.f;
+      den = __builtin_fmaf(sc, dx, den);
+      const f32x4 ox = *(const f32x4*)(red + (x * 16 + r) * D + 4 * q4);
+      acc[0] = __builtin_fmaf(sc, ox[0], acc[0]);
+      acc[1] = __builtin_fmaf(sc, ox[1], acc[1]);
+      acc[2] = __builtin_fmaf(sc, ox[2], acc[2]);
+      acc[3] = __builtin_fmaf(sc, ox[3], acc[3]);
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const float lse_nat = den > 0.f ? (msub + __builtin_log2f(den)) * kLn2 : kNegInf;
+    const int rt = r / G;
+    const int64_t orow = ((int64_t)b * a.q_len + rt) * Hq + g * G + (r - rt * G);
+    if constexpr (DIRECT) {
+      u32x2 pk2;
+      pk2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      pk2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      *(u32x2*)((__bf16*)a.out + orow * D + 4 * q4) = pk2;
+      if (q4 == 0 && a.lse != nullptr) a.lse[orow] = lse_nat;
+    } else {
+      *(f32x4*)(a.part_o + (orow * S + slot) * D + 4 * q4) =
+          f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      if (q4 == 0) a.part_lse[orow * S + slot] = lse_nat;
+    }
+  }
+}
+
 // Merge: D/4 lanes per row, each owning four consecutive head dims, so a row's
 // partial outputs are read as whole 16-byte vectors and a wavefront covers 256/D rows.
 // Slots are taken four at a time: the four loads are issued together, and a group
@@ -340,6 +605,17 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int w, dim3 grid, hipStre
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
                                bool direct, hipStream_t stream) {
+  if (a.chunk_waves > 1) {  // q_len * G <= 16: chunk-wave kernel, one row group
+    dim3 grid(a.num_slots, num_kv_heads, batch);
+    if (head_dim == 64) {
+      if (direct) hipLaunchKernelGGL((decode_cw_kernel<64, 4, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((decode_cw_kernel<64, 4, false>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (direct) hipLaunchKernelGGL((decode_cw_kernel<128, 2, true>), grid, dim3(128), 0, stream, a);
+      else hipLaunchKernelGGL((decode_cw_kernel<128, 2, false>), grid, dim3(128), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   const int w = decode_waves(a.q_len * a.group);
   dim3 grid(a.num_slots, num_kv_heads * a.row_groups, batch);
   if (head_dim == 64)

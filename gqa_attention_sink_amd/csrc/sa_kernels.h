@@ -39,7 +39,8 @@ struct DecodeArgs {
   int32_t group;       // query heads per KV head
   int32_t row_groups;  // ceil(q_len * group / (16 * decode_waves(q_len * group)))
   int32_t num_splits;  // 0 = planner
-  int32_t num_slots;   // chunk slots per row in the partial layout
+  int32_t num_slots;   // partial slots per row (chunk groups of chunk_waves chunks)
+  int32_t chunk_waves; // chunks one workgroup takes together (1: split kernel; 4 or 2: chunk-wave kernel)
   int32_t causal;
   float scale_log2;
   float* part_o;       // [rows, num_slots, D]   (split mode)
@@ -50,6 +51,12 @@ struct DecodeArgs {
 
 // Wavefronts per decode workgroup (16 query rows each) for M rows sharing a KV head.
 inline int decode_waves(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+
+// Chunks per decode workgroup: with at most 16 rows per KV head the chunk-wave kernel
+// takes 4 (head_dim 64) or 2 (head_dim 128) chunks per workgroup, one per wavefront.
+inline int decode_chunk_waves(int rows, int head_dim) {
+  return rows <= 16 ? (head_dim == 64 ? 4 : 2) : 1;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
                           hipStream_t stream);

@@ -35,10 +35,9 @@ _SIGS = {
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
-    "sink_attn_decode_workspace_bytes": (ctypes.c_size_t, [
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32]),
-    "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
+    "sink_attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
+    "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32] * 6),
+    "sink_attn_decode_chunks_per_slot": (ctypes.c_int32, [ctypes.c_int32] * 4),
     "sink_attn_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -148,21 +147,29 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     return out, lse
 
 
-def decode_num_slots(max_kv_len: int, num_splits: int = 0) -> int:
-    return int(load().sink_attn_decode_num_slots(int(max_kv_len), int(num_splits)))
+def decode_chunks_per_slot(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    """Consecutive plan chunks whose merged state one partial slot holds."""
+    return int(load().sink_attn_decode_chunks_per_slot(q_len, num_q_heads, num_kv_heads, head_dim))
 
 
-def decode_workspace_bytes(batch: int, q_len: int, num_q_heads: int, head_dim: int,
-                           max_kv_len: int, num_splits: int = 0) -> int:
-    return int(load().sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, head_dim,
-                                                       int(max_kv_len), int(num_splits)))
+def decode_num_slots(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     max_kv_len: int, num_splits: int = 0) -> int:
+    return int(load().sink_attn_decode_num_slots(q_len, num_q_heads, num_kv_heads, head_dim,
+                                                 int(max_kv_len), int(num_splits)))
 
 
-def decode_workspace(batch: int, q_len: int, num_q_heads: int, head_dim: int,
-                     max_kv_len: int, num_splits: int = 0, device="cuda"):
+def decode_workspace_bytes(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_kv_len: int, num_splits: int = 0) -> int:
+    return int(load().sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
+                                                       head_dim, int(max_kv_len), int(num_splits)))
+
+
+def decode_workspace(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, max_kv_len: int, num_splits: int = 0, device="cuda"):
     """A uint8 workspace for decode() of these sizes (contents need no initialisation);
     stream-ordered calls of any sizes it fits may share it."""
-    nbytes = decode_workspace_bytes(batch, q_len, num_q_heads, head_dim, max_kv_len, num_splits)
+    nbytes = decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                    max_kv_len, num_splits)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
@@ -191,9 +198,9 @@ def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float]
     b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
     sinks = _sinks_arg(sinks, hq, q.device)
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    nbytes = decode_workspace_bytes(b, ql, hq, d, max_kv_len, num_splits)
+    nbytes = decode_workspace_bytes(b, ql, hq, hkv, d, max_kv_len, num_splits)
     if workspace is None:
-        workspace = decode_workspace(b, ql, hq, d, max_kv_len, num_splits, q.device)
+        workspace = decode_workspace(b, ql, hq, hkv, d, max_kv_len, num_splits, q.device)
     else:
         _dev_tensor(workspace, torch.uint8, "workspace")
     if out is None:
@@ -214,12 +221,13 @@ def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float]
 def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
                    causal: bool = True, num_splits: int = 0, part_o=None, part_lse=None):
     """First stage of decode alone.  Returns (part_o [B*q_len*Hq, S, D] fp32,
-    part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(max_kv_len, num_splits)."""
+    part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(q_len, Hq, Hkv, D, max_kv_len,
+    num_splits); slot j holds plan chunks [j*C, j*C + C), C = decode_chunks_per_slot(...)."""
     lib = load()
     b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
     sinks = _sinks_arg(sinks, hq, q.device)
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    s = decode_num_slots(max_kv_len, num_splits)
+    s = decode_num_slots(ql, hq, hkv, d, max_kv_len, num_splits)
     rows = b * ql * hq
     if part_o is None:
         part_o = torch.empty((rows, s, d), dtype=torch.float32, device=q.device)

@@ -87,9 +87,11 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
  *             sits at position Lk - q_len + t; with causal=1 it sees keys <= that
  *             position (causal within the draft).
  *  max_kv_len host upper bound of kv_indptr[b+1]-kv_indptr[b].
- *  num_splits 0 = planner: clamp(ceil(Lk/256), 4, 16) chunks for each sequence;
- *             k in 1..64 = exactly k chunks per sequence.  A chunk holds
- *             ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
+ *  num_splits 0 = planner: n = ceil(Lk/256) rounded up to a multiple of C and clamped
+ *             to [4, 16] chunks for each sequence, where C =
+ *             sink_attn_decode_chunks_per_slot(...) is the number of chunks one
+ *             workgroup takes together; k in 1..64 = exactly k chunks per sequence.  A
+ *             chunk holds ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
  *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,
  *             256-byte aligned; contents need no initialisation.  Calls that share one
  *             workspace must be stream-ordered.
@@ -104,21 +106,31 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
                      size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
- * invalid).  Holds fp32 partial outputs and partial lse for every (row, chunk). */
+ * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot). */
 size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
-                                        int32_t head_dim, int32_t max_kv_len,
-                                        int32_t num_splits);
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_kv_len, int32_t num_splits);
 
-/* Number of chunk slots per row the decode path uses (the S of the partial layout). */
-int32_t sink_attn_decode_num_slots(int32_t max_kv_len, int32_t num_splits);
+/* Chunks per partial slot, C: with q_len * (num_q_heads/num_kv_heads) <= 16 rows per KV
+ * head one workgroup streams C consecutive chunks in parallel (one wavefront each, C = 4
+ * for head_dim 64 and 2 for 128) and merges them before writing; otherwise C = 1.
+ * 0 if the arguments are invalid. */
+int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim);
+
+/* Partial slots per row the decode path uses (the S of the partial layout):
+ * ceil(n_max / C) with n_max the planner's chunk count at max_kv_len.  0 if invalid. */
+int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_kv_len, int32_t num_splits);
 
 /*
- * First stage of sink_attn_decode on its own: the split kernel writes, for every row
- * r = (b*q_len + t)*num_q_heads + h and chunk slot c < S, the chunk's normalised
- * output part_o[r][c][0..head_dim) (fp32) and its natural-log partition function
- * part_lse[r][c] (fp32; -inf for an empty chunk or an unused slot; chunk 0 includes
- * the sink).  S = sink_attn_decode_num_slots(max_kv_len, num_splits).  Exported so the
- * per-chunk partials can be checked and timed; sink_attn_decode = this + merge.
+ * First stage of sink_attn_decode on its own: for every row
+ * r = (b*q_len + t)*num_q_heads + h and slot j < S, the normalised output
+ * part_o[r][j][0..head_dim) (fp32) and natural-log partition function part_lse[r][j]
+ * (fp32; -inf when empty) of the keys of plan chunks [j*C, j*C + C) together (chunk 0
+ * includes the sink).  S = sink_attn_decode_num_slots(...), C =
+ * sink_attn_decode_chunks_per_slot(...).  Exported so the partials can be checked and
+ * timed; sink_attn_decode = this + merge (with S = 1 the kernel writes the result).
  */
 int sink_attn_decode_partial(const void* q, const void* k, const void* v,
                              const float* sinks, const int32_t* kv_indptr, int32_t batch,

@@ -35,7 +35,8 @@ def _declared():
 def test_header_declares_entry_points():
     names = _declared()
     for n in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_workspace_bytes",
-              "sink_attn_merge", "sink_attn_status_str", "sink_attn_decode_partial"):
+              "sink_attn_merge", "sink_attn_status_str", "sink_attn_decode_partial",
+              "sink_attn_decode_num_slots", "sink_attn_decode_chunks_per_slot"):
         assert n in names
 
 
@@ -59,8 +60,9 @@ def _prefill(lib, **kw):
 
 
 def _decode(lib, **kw):
+    # 32 rows per KV head: one chunk per wavefront, 4 slots, so a workspace is needed
     a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, ind=FAKE, batch=2, ql=1, tk=64, maxk=32,
-             hq=8, hkv=2, d=64, scale=0.125, causal=1, ns=0, ws=None, wsb=0, out=FAKE, lse=None)
+             hq=64, hkv=2, d=64, scale=0.125, causal=1, ns=0, ws=None, wsb=0, out=FAKE, lse=None)
     a.update(kw)
     return lib.sink_attn_decode(a["q"], a["k"], a["v"], a["sinks"], a["ind"], a["batch"],
                                 a["ql"], a["tk"], a["maxk"], a["hq"], a["hkv"], a["d"],
@@ -114,10 +116,24 @@ def test_merge_validation(lib):
 
 def test_planner_slots(lib):
     ns = lib.sink_attn_decode_num_slots
-    assert ns(8192, 0) == 16 and ns(1024, 0) == 4 and ns(100, 0) == 4 and ns(0, 0) == 4
-    assert ns(2049, 0) == 9 and ns(4097, 0) == 16 and ns(100000, 0) == 16
-    assert ns(32768, 32) == 32 and ns(10, 1) == 1
-    assert ns(10, 65) == 0 and ns(-1, 0) == 0
+    cps = lib.sink_attn_decode_chunks_per_slot
+    # one wavefront per chunk when q_len*G > 16 (here 4 x 8 = 32 rows): slots = chunks
+    assert cps(4, 32, 4, 64) == 1
+    assert ns(4, 32, 4, 64, 8192, 0) == 16 and ns(4, 32, 4, 64, 1024, 0) == 4
+    assert ns(4, 32, 4, 64, 100, 0) == 4 and ns(4, 32, 4, 64, 0, 0) == 4
+    assert ns(4, 32, 4, 64, 2049, 0) == 9 and ns(4, 32, 4, 64, 100000, 0) == 16
+    assert ns(4, 32, 4, 64, 32768, 32) == 32 and ns(4, 32, 4, 64, 10, 1) == 1
+    # <= 16 rows: 4 chunks per slot (head_dim 64) or 2 (head_dim 128); the planner rounds
+    # ceil(Lk/256) up to a multiple of that before clamping to [4, 16]
+    assert cps(1, 64, 8, 64) == 4 and cps(1, 64, 8, 128) == 2 and cps(2, 16, 2, 64) == 4
+    assert ns(1, 64, 8, 64, 8192, 0) == 4 and ns(1, 64, 8, 64, 1024, 0) == 1
+    assert ns(1, 64, 8, 64, 1025, 0) == 2 and ns(1, 64, 8, 64, 3000, 0) == 3
+    assert ns(1, 64, 8, 128, 2049, 0) == 5 and ns(1, 64, 8, 128, 100, 0) == 2
+    assert ns(1, 64, 8, 64, 32768, 7) == 2 and ns(1, 64, 8, 64, 10, 1) == 1
+    # invalid arguments
+    assert ns(1, 64, 8, 64, 10, 65) == 0 and ns(1, 64, 8, 64, -1, 0) == 0
+    assert ns(0, 64, 8, 64, 10, 0) == 0 and ns(1, 64, 7, 64, 10, 0) == 0
+    assert ns(1, 64, 8, 96, 10, 0) == 0 and cps(5, 64, 8, 64) == 0
 
 
 def test_workspace_bytes(lib):
@@ -126,9 +142,12 @@ def test_workspace_bytes(lib):
     o = rows * s * d * 4
     o = (o + 255) // 256 * 256
     expect = (o + rows * s * 4 + 255) // 256 * 256
-    assert wb(256, 4, 64, 128, 32768, 32) == expect
-    assert wb(64, 1, 64, 64, 8192, 0) >= 64 * 64 * 16 * 65 * 4
-    assert wb(0, 1, 8, 64, 10, 0) == 0 and wb(1, 5, 8, 64, 10, 0) == 0 and wb(1, 1, 8, 96, 10, 0) == 0
+    assert wb(256, 4, 64, 4, 128, 32768, 32) == expect
+    rows, s, d = 64 * 64, 4, 64                      # 16 planned chunks in 4 slots
+    o = (rows * s * d * 4 + 255) // 256 * 256
+    assert wb(64, 1, 64, 8, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
+    assert wb(0, 1, 8, 8, 64, 10, 0) == 0 and wb(1, 5, 8, 8, 64, 10, 0) == 0
+    assert wb(1, 1, 8, 8, 96, 10, 0) == 0 and wb(1, 1, 8, 3, 64, 10, 0) == 0
 
 
 def test_status_strings(lib):

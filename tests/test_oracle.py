@@ -202,6 +202,11 @@ def test_plan_chunks_rule():
         assert all(x % 32 == 0 or x == lk for x in b)
     assert len(plan_chunks(1024, 0)) - 1 == 4 and len(plan_chunks(4096, 0)) - 1 == 16
     assert plan_chunks(32768, 32) == list(range(0, 32768, 1024)) + [32768]
+    # grouped planning: the count is a multiple of the group size before the clamp
+    for lk, grp, want in ((1024, 4, 4), (1025, 4, 8), (3000, 4, 12), (9000, 4, 16),
+                          (100, 4, 4), (2049, 2, 10), (100, 2, 4), (5000, 2, 16)):
+        assert len(plan_chunks(lk, 0, multiple=grp)) - 1 == want
+    assert plan_chunks(777, 7, multiple=4) == plan_chunks(777, 7)
 
 
 # ---------------------------------------------------------------- P8 GQA == MHA

@@ -213,8 +213,9 @@ def test_decode_spec_full_sampled(sa):
 
 @pytest.mark.parametrize("ns", [0, 4, 7])
 def test_decode_partials_match_oracle_chunks(sa, ns):
-    """Per-chunk partials of the split kernel against the oracle's chunk form with the
-    same chunk plan: checks the planner, the sink in chunk 0 only and empty chunks."""
+    """Per-slot partials (each slot = a group of consecutive plan chunks) against the
+    oracle's chunk form with the same plan: checks the planner, the grouping, the sink
+    in chunk 0 only and empty chunks."""
     lens = [1, 40, 600, 2000, 5000]
     w = wl.make_decode(lens, 2, 16, 4, 64, ("normal", 1, 2), 0.125, True, ns, seed=300 + ns,
                        device="cuda")
@@ -223,9 +224,12 @@ def test_decode_partials_match_oracle_chunks(sa, ns):
                                True, ns)
     torch.cuda.synchronize()
     s = pl.shape[1]
+    cps = sa.decode_chunks_per_slot(2, 16, 4, 64)
+    assert cps == 4  # 8 rows per KV head: four chunks per slot
     bounds = []
     for lk in lens:
-        bd = oracle.plan_chunks(lk, ns)
+        bd = oracle.plan_chunks(lk, ns, multiple=cps)
+        bd = bd[::cps] if (len(bd) - 1) % cps == 0 else bd[::cps] + [lk]  # slot = chunk group
         bounds.append(bd + [lk] * (s + 1 - len(bd)))
     cu_q = torch.arange(len(lens) + 1, dtype=torch.int32) * 2
     q2 = w.q.reshape(-1, 16, 64)
@@ -276,7 +280,7 @@ def test_decode_workspace_reuse(sa):
                          0, seed=410, device="cuda")
     small = wl.make_decode([33, 700, 5], 1, 8, 1, 128, ("normal", 0, 2), 1 / math.sqrt(128),
                            True, 7, seed=411, device="cuda")
-    nb = max(sa.decode_workspace_bytes(w.batch, w.q_len, w.hq, w.d, w.max_kv, w.num_splits)
+    nb = max(sa.decode_workspace_bytes(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
              for w in (big, small))
     ws = torch.full((nb,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage contents
     refs = {id(w): _oracle_decode(w) for w in (big, small)}

@@ -3,7 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step is one pass of the whole decode hot path (split-KV kernel + log-sum-exp
-merge) over the gpt-oss-like decode batch (64 sequences, 1 query token, Hq 64 over
+merge of its partial slots) over the gpt-oss-like decode batch (64 sequences, 1 query token, Hq 64 over
 Hkv 8, head_dim 64, KV lengths uniform in [1024, 8192]), with inputs resident in HBM.
 Before every step a 512 MiB read (a sum over a scratch buffer) evicts the 256 MB
 Infinity Cache and the L2s with clean lines, so each step streams its K/V from HBM and
@@ -251,6 +251,9 @@ def main():
     split_bytes = decode_bytes(w, split_only=True)
     value = nbytes / (r["full_ms"] * 1e-3) / 1e9
     split_gbs = split_bytes / (r["split_ms"] * 1e-3) / 1e9
+    # the dominant kernel: chunk-wave kernel when a workgroup merges several chunks
+    kname = ("decode_cw_kernel" if sa.decode_chunks_per_slot(w.q_len, w.hq, w.hkv, w.d) > 1
+             else "decode_split_kernel")
     line = {
         "metric": "sink-attn decode HBM GB/s (and prefill TFLOP/s) on 1 MI355X, % of peak",
         "value": round(value, 2),
@@ -271,10 +274,10 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_min": round(r["full_ms_min"], 4),
         "wall_ms_per_step_incl_flush": round(r["wall_s"] * 1e3 / args.steps, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic_for("decode_split_kernel", w.name),
+                     "traffic": _traffic_for(kname, w.name),
                      "algorithmic_bytes_per_launch": split_bytes,
                      "avg_launch_ms": round(r["split_ms"], 4),
                      "merge_ms": round(r["merge_ms"], 4)},

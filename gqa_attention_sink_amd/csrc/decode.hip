@@ -307,12 +307,26 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
   constexpr int ROW = D * 2;
   constexpr int CPR = D / 8;
   constexpr int STEP = 32;
-  constexpr int NST = 4;                  // per-wavefront ring depth
+  // Per-wavefront ring depth: 2 stages keep the workgroup under half the LDS, so two
+  // workgroups share a CU and one's start-up and drain overlap the other's stream
+  // (measured faster than 4 stages at one workgroup per CU).
+  constexpr int NST = 2;
   constexpr int SB = STEP * ROW;
   constexpr int NDMA = SB / (64 * 16);    // copies per lane per tensor per stage
   static_assert(CW * NST * 2 * SB <= 160 * 1024, "LDS");
   static_assert(CW * 16 * (D + 2) * 4 <= CW * NST * 2 * SB, "combine scratch fits the rings");
-  __shared__ __attribute__((aligned(16))) unsigned char ring[CW][NST][2][SB];
+  // One LDS object holds the rings, the Q tiles and the sinks (with separate objects
+  // the compiler cannot tell the ring reads from the copies in flight and waits for all
+  // of them before every stage).
+  struct Smem {
+    unsigned char ring[CW][NST][2][SB];
+    unsigned char q[CW][16 * ROW];
+    float sink[CW][64];
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  auto& ring = sm.ring;
+  auto& q_lds = sm.q;
+  auto& sink_lds = sm.sink;
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -364,17 +378,36 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
     }
   };
 
-  const uint32_t qbytes = (uint32_t)(a.q_len * Hq * ROW);
-  const __amdgpu_buffer_rsrc_t qr =
-      make_rsrc((const __bf16*)a.q + (size_t)b * a.q_len * Hq * D, qbytes);
+  // The 16 Q rows and the sinks arrive through asynchronous copies into LDS issued
+  // ahead of the ring prologue, so no register load is pending when the stage loop
+  // starts (a pending one would make the loop wait for the whole prologue).
+  {
+    const uint32_t qbytes = (uint32_t)(a.q_len * Hq * ROW);
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc((const __bf16*)a.q + (size_t)b * a.q_len * Hq * D, qbytes);
+#pragma unroll
+    for (int i = 0; i < 16 * CPR / 64; ++i) {
+      const int p = i * 64 + lane;            // 16-byte piece of the [16][D] Q tile
+      const int r = p / CPR;
+      const int rt = r / G;
+      const int rh = g * G + (r - rt * G);
+      const uint32_t off = (r < M) ? (uint32_t)((rt * Hq + rh) * ROW + (p - r * CPR) * 16) : qbytes;
+      dma16(qr, off, &q_lds[w][i * 1024]);
+    }
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.sinks, a.sinks != nullptr ? (uint32_t)Hq * 4 : 0u);
+    dma4(sr, (c == 0 && row_ok) ? (uint32_t)row_h * 4 : kNoRead, &sink_lds[w][0]);
+  }
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue(st);
+  wait_vmcnt<(NST - 1) * 2 * NDMA>();  // the Q rows and sinks (issued first) have landed
+
+  // Q^T operands (B of S^T): lane holds Q[row][ks*32 + cg*8 .. +8]; zero for padding.
   bf16x8 qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)((row_t * Hq + row_h) * ROW + (ks * 32 + cg * 8) * 2);
-    qop[ks] = as_bf16x8(load16(qr, row_ok ? off : qbytes));
-  }
-  float sig = kNegInf;
-  if (c == 0 && a.sinks != nullptr && row_ok) sig = a.sinks[row_h] * kLog2e;
+  for (int ks = 0; ks < KS; ++ks)
+    qop[ks] = *(const bf16x8*)&q_lds[w][l16 * ROW + (ks * 32 + cg * 8) * 2];
+  const float sig = (c == 0 && a.sinks != nullptr && row_ok) ? sink_lds[w][lane] * kLog2e : kNegInf;
   float m = sig;
   float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;
   f32x4 o[DPL];
@@ -385,14 +418,13 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
   const int causal_first_masked = a.causal ? (lk - a.q_len + 1) : 0x7fffffff;
   const int lim = min(ke - 1, a.causal ? lk - a.q_len + row_t : 0x7fffffff);
 
-#pragma unroll
-  for (int st = 0; st < NST - 1; ++st) issue(st);
-
   for (int st = 0; st < nsteps; ++st) {
-    // stage st has landed once only the NST-2 stages issued after it are pending; the
-    // ring is this wavefront's own, and its reads of slot (st-1) have completed
-    wait_vmcnt<(NST - 2) * 2 * NDMA>();
+    // The ring is this wavefront's own and its reads of slot (st-1) completed in the
+    // previous iteration, so that slot is refilled before waiting: NST stages are in
+    // flight during the wait.  Stage st has landed once only the NST-1 stages issued
+    // after it are pending.
     issue(st + NST - 1);
+    wait_vmcnt<(NST - 1) * 2 * NDMA>();
 
     const unsigned char* kbuf = my[st % NST][0];
     const unsigned char* vbuf = my[st % NST][1];

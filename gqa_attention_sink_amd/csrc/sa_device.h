@@ -53,6 +53,16 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, vo
       r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
 }
 
+// An offset no bounded view reaches (views are < 2^31 bytes): the copy reads nothing
+// and writes zeros.
+constexpr uint32_t kNoRead = 0x80000000u;
+
+// Asynchronous 4-byte copy global -> LDS: lane i writes its 4 bytes at base + 4*i.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 4, off, 0, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wavefront are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

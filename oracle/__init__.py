@@ -12,3 +12,9 @@ from .sink_attention import (  # noqa: F401
     plan_chunks,
     flops_causal,
 )
+from .paged_kv import (  # noqa: F401
+    paged_seq_lens,
+    gather_paged,
+    kv_append,
+    sink_attention_decode_paged,
+)

@@ -9,9 +9,11 @@ from .sink_attn import (  # noqa: F401
     decode,
     decode_chunks_per_slot,
     decode_num_slots,
+    decode_paged,
     decode_partial,
     decode_workspace,
     decode_workspace_bytes,
+    kv_append,
     load,
     merge,
     prefill,

@@ -89,12 +89,47 @@ sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const fl
   const int w = sa::decode_waves(rows);
   a.row_groups = (rows + 16 * w - 1) / (16 * w);
   a.num_splits = num_splits;
+  a.num_kv_heads = hkv;
   a.chunk_waves = chunk_waves(q_len, hq, hkv, d);
   a.num_slots = planned_slots(max_kv_len, num_splits, a.chunk_waves);
   a.causal = causal;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return a;
 }
+
+// Split kernel (+ merge when there is more than one slot) for contiguous or paged KV.
+int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
+               const int32_t* page_ids, void* workspace, size_t workspace_bytes, void* out,
+               float* lse, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (a.num_slots == 1) {  // one slot per row: the split kernel writes the result
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, page_ids, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  }
+  const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
+                                                       head_dim, max_kv_len, num_splits);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SINK_ATTN_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  int64_t obytes = rows * a.num_slots * head_dim * 4;
+  obytes = (obytes + 255) & ~(int64_t)255;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + obytes);
+  hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, page_ids, st);
+  if (e != hipSuccess) return hip_fail(e);
+  e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return SINK_ATTN_OK;
+}
+
+// Paged caches: page_size a multiple of 16 (a 32-key stage then spans at most two pages
+// and no copy instruction straddles a page boundary).
+constexpr int kMaxPageSize = 4096;
+inline bool page_size_ok(int32_t ps) { return ps >= 16 && ps <= kMaxPageSize && ps % 16 == 0; }
 
 }  // namespace
 
@@ -212,7 +247,7 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
                                    num_splits);
     a.part_o = part_o;
     a.part_lse = part_lse;
-    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, (hipStream_t)stream);
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {
@@ -235,26 +270,76 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
     sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
-    hipStream_t st = (hipStream_t)stream;
-    if (a.num_slots == 1) {  // one chunk per sequence: the split kernel writes the result
-      a.out = out;
-      a.lse = lse;
-      hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, st);
-      if (e != hipSuccess) return hip_fail(e);
-      return SINK_ATTN_OK;
-    }
-    const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
-                                                         head_dim, max_kv_len, num_splits);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
-      return SINK_ATTN_ERR_WORKSPACE;
-    const int64_t rows = (int64_t)batch * q_len * num_q_heads;
-    int64_t obytes = rows * a.num_slots * head_dim * 4;
-    obytes = (obytes + 255) & ~(int64_t)255;
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + obytes);
-    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, st);
-    if (e != hipSuccess) return hip_fail(e);
-    e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
+    return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                      num_splits, nullptr, workspace, workspace_bytes, out, lse, stream);
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                           const float* sinks, const int32_t* kv_page_indptr,
+                           const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                           int32_t batch, int32_t q_len, int64_t num_page_entries,
+                           int64_t num_pages, int32_t page_size, int32_t max_kv_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           float sm_scale, int32_t causal, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream) {
+  try {
+    if (!kv_page_indices || !kv_last_page_len) return SINK_ATTN_ERR_INVALID_ARG;
+    if (num_page_entries < 0 || num_pages < 1) return SINK_ATTN_ERR_INVALID_ARG;
+    if (!page_size_ok(page_size)) return SINK_ATTN_ERR_UNSUPPORTED;
+    int rc = check_decode_args(q, k_cache, v_cache, kv_page_indptr, batch, q_len, 0, max_kv_len,
+                               num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
+    if (rc != SINK_ATTN_OK) return rc;
+    if (!out) return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::DecodeArgs a = decode_args(q, k_cache, v_cache, sinks, nullptr, q_len, 0, max_kv_len,
+                                   num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
+                                   num_splits);
+    a.kv_page_indptr = kv_page_indptr;
+    a.kv_last_page_len = kv_last_page_len;
+    a.num_page_entries = num_page_entries;
+    a.num_pages = num_pages;
+    a.page_size = page_size;
+    return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                      num_splits, kv_page_indices, workspace, workspace_bytes, out, lse, stream);
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
+                        const int32_t* kv_page_indptr, const int32_t* kv_page_indices,
+                        const int32_t* kv_last_page_len, int32_t batch, int32_t max_append_len,
+                        int64_t total_new, int64_t num_page_entries, int64_t num_pages,
+                        int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                        void* k_cache, void* v_cache, void* stream) {
+  try {
+    if (!k_new || !v_new || !append_indptr || !kv_page_indptr || !kv_page_indices ||
+        !kv_last_page_len || !k_cache || !v_cache)
+      return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch < 1 || max_append_len < 0 || total_new < 0 || num_page_entries < 0 ||
+        num_pages < 1 || num_kv_heads < 1)
+      return SINK_ATTN_ERR_INVALID_ARG;
+    if (!page_size_ok(page_size) || !dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (max_append_len == 0 || total_new == 0) return SINK_ATTN_OK;
+    sa::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.append_indptr = append_indptr;
+    a.kv_page_indptr = kv_page_indptr;
+    a.kv_last_page_len = kv_last_page_len;
+    a.total_new = total_new;
+    a.num_page_entries = num_page_entries;
+    a.num_pages = num_pages;
+    a.page_size = page_size;
+    a.num_kv_heads = num_kv_heads;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    hipError_t e = sa::launch_kv_append(a, head_dim, batch, max_append_len, kv_page_indices,
+                                        (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {

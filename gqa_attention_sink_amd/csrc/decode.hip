@@ -38,6 +38,39 @@ __device__ __forceinline__ int seq_begin(const DecodeArgs& a, int b) {
 __device__ __forceinline__ int seq_end(const DecodeArgs& a, int b) {
   return (int)min<int64_t>(max(a.kv_indptr[b + 1], seq_begin(a, b)), a.total_kv);
 }
+// Paged sequence b: its first page-list entry and its length, clamped so that every
+// page-list read stays inside the list.
+__device__ __forceinline__ int page_begin(const DecodeArgs& a, int b) {
+  return (int)min<int64_t>(max(a.kv_page_indptr[b], 0), a.num_page_entries);
+}
+__device__ __forceinline__ int paged_len(const DecodeArgs& a, int b, int e0) {
+  const int np = (int)min<int64_t>(max(a.kv_page_indptr[b + 1], e0), a.num_page_entries) - e0;
+  if (np == 0) return 0;
+  const int last = min(max(a.kv_last_page_len[b], 1), a.page_size);
+  return (int)min<int64_t>((int64_t)(np - 1) * a.page_size + last, 1 << 24);
+}
+// Bounded views of K and V for the rows of page-list slot `ps_slot` of a paged sequence
+// that lie before key `ke` (<= the sequence length): page ids are read with scalar
+// loads and clamped to the cache, rows at or past ke read zeros.
+template <int D>
+__device__ __forceinline__ void page_views(const DecodeArgs& a, const int32_t* __restrict__ page_ids,
+                                           int e0, int g, int ps_slot, int ke,
+                                           __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr) {
+  const int ps = a.page_size;
+  const int rows = min(max(ke - ps_slot * ps, 0), ps);
+  if (rows == 0) {  // nothing of this page is read (also covers empty sequences)
+    kr = make_rsrc(a.k, 0u);
+    vr = make_rsrc(a.v, 0u);
+    return;
+  }
+  // rows > 0 implies ps_slot * ps < ke <= lk, so the entry lies inside the sequence's list
+  int64_t pid = page_ids[e0 + ps_slot];
+  pid = min<int64_t>(max<int64_t>(pid, 0), a.num_pages - 1);
+  const size_t base = ((size_t)pid * a.num_kv_heads + g) * ps * D;
+  kr = make_rsrc((const __bf16*)a.k + base, (uint32_t)rows * D * 2);
+  vr = make_rsrc((const __bf16*)a.v + base, (uint32_t)rows * D * 2);
+}
+
 __device__ __forceinline__ int chunk_len(int lk, int n) {
   int cl = lk > 0 ? (lk + n - 1) / n : 0;
   return (cl + 31) & ~31;
@@ -61,8 +94,9 @@ __device__ __forceinline__ int dswz(int row) {
 // chunk); wavefront w owns 16 query rows.  The chunk's K and V stream from HBM into an
 // NST-stage LDS ring with asynchronous 16-byte buffer->LDS copies (no registers),
 // NST-1 stages ahead of the compute, and every wavefront reads each stage from LDS.
-template <int D, int W, bool DIRECT>
-__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
+template <int D, int W, bool DIRECT, bool PAGED>
+__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
+                                                              const int32_t* __restrict__ page_ids) {
   constexpr int KS = D / 32;              // k-steps (32 head dims) of S^T
   constexpr int DPL = D / 16;             // head dims per lane per V row read = O^T d-tiles
   constexpr int ROW = D * 2;              // bytes per K/V row
@@ -89,8 +123,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   const int Hq = a.num_q_heads;
   const int M = a.q_len * G;
 
-  const int kv0 = seq_begin(a, b);
-  const int lk = seq_end(a, b) - kv0;
+  int kv0 = 0, e0 = 0, lk;
+  if constexpr (PAGED) {
+    e0 = page_begin(a, b);
+    lk = paged_len(a, b, e0);
+  } else {
+    kv0 = seq_begin(a, b);
+    lk = seq_end(a, b) - kv0;
+  }
   const int n = plan_chunks(lk, a.num_splits, 1);
   const int cl = chunk_len(lk, n);
   const int S = a.num_slots;
@@ -110,22 +150,46 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   const int ke = min(lk, kb + cl);
   const int nsteps = (ke - kb + STEP - 1) / STEP;
 
-  // K/V of this chunk: loads past the chunk end return zero.
-  const size_t head_base = ((size_t)g * a.total_kv + kv0 + kb) * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, (uint32_t)(ke - kb) * ROW);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, (uint32_t)(ke - kb) * ROW);
+  // K/V of this chunk: loads past the chunk end return zero.  Contiguous HND: one view
+  // of the chunk.  Paged: a 32-key stage spans at most two pages (page_size is a
+  // multiple of 16), and each copy instruction's rows lie inside one of them.
+  const size_t head_base = PAGED ? 0 : ((size_t)g * a.total_kv + kv0 + kb) * D;
+  const uint32_t chunk_bytes = PAGED ? 0u : (uint32_t)(ke - kb) * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, chunk_bytes);
   auto issue = [&](int st) {
     unsigned char* kbuf = ring[st % NST][0];
     unsigned char* vbuf = ring[st % NST][1];
+    if constexpr (PAGED) {
+      const int t0 = kb + st * STEP;          // the stage's first key
+      const int ps = a.page_size;
+      const int pa = t0 / ps;
+      __amdgpu_buffer_rsrc_t ka, va, kb2, vb2;
+      page_views<D>(a, page_ids, e0, g, pa, ke, ka, va);
+      page_views<D>(a, page_ids, e0, g, pa + 1, ke, kb2, vb2);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int blk = i * W + wave;           // 1 KiB block of the stage this wave fills
-      const int p = blk * 64 + lane;          // 16-byte chunk index inside the stage
-      const int row = p / CPR;
-      const int cc = p - row * CPR;
-      const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
-      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
-      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+      for (int i = 0; i < NDMA; ++i) {
+        const int blk = i * W + wave;
+        const int p = blk * 64 + lane;
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const int tok0 = t0 + blk * (64 / CPR);  // first row of this copy instruction
+        const bool second = tok0 / ps != pa;
+        const uint32_t rbase = (uint32_t)(t0 + row - (pa + (second ? 1 : 0)) * ps) * ROW;
+        dma16(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+        dma16(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int blk = i * W + wave;           // 1 KiB block of the stage this wave fills
+        const int p = blk * 64 + lane;          // 16-byte chunk index inside the stage
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
+        dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+        dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+      }
     }
   };
 
@@ -300,8 +364,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 // key axis merge by their log-sum-exp; the sink sits in chunk 0).  One partial (or,
 // with a single slot, the final output) leaves the workgroup instead of CW of them,
 // which cuts the partial traffic written during the KV stream and read by the merge.
-template <int D, int CW, bool DIRECT>
-__global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
+template <int D, int CW, bool DIRECT, bool PAGED>
+__global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
+                                                            const int32_t* __restrict__ page_ids) {
   constexpr int KS = D / 32;
   constexpr int DPL = D / 16;
   constexpr int ROW = D * 2;
@@ -340,8 +405,14 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
   const int M = a.q_len * G;
   const int S = a.num_slots;
 
-  const int kv0 = seq_begin(a, b);
-  const int lk = seq_end(a, b) - kv0;
+  int kv0 = 0, e0 = 0, lk;
+  if constexpr (PAGED) {
+    e0 = page_begin(a, b);
+    lk = paged_len(a, b, e0);
+  } else {
+    kv0 = seq_begin(a, b);
+    lk = seq_end(a, b) - kv0;
+  }
   const int n = plan_chunks(lk, a.num_splits, CW);
   const int cl = chunk_len(lk, n);
 
@@ -360,21 +431,43 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a) {
   const int ke = (c < n) ? min(lk, kb + cl) : kb;
   const int nsteps = (ke - kb + STEP - 1) / STEP;
 
-  const size_t head_base = ((size_t)g * a.total_kv + kv0 + kb) * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, (uint32_t)(ke - kb) * ROW);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, (uint32_t)(ke - kb) * ROW);
+  // K/V views as in the split kernel (one chunk view, or per-page views when paged).
+  const size_t head_base = PAGED ? 0 : ((size_t)g * a.total_kv + kv0 + kb) * D;
+  const uint32_t chunk_bytes = PAGED ? 0u : (uint32_t)(ke - kb) * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, chunk_bytes);
   unsigned char (*my)[2][SB] = ring[w];
   auto issue = [&](int st) {
     unsigned char* kbuf = my[st % NST][0];
     unsigned char* vbuf = my[st % NST][1];
+    if constexpr (PAGED) {
+      const int t0 = kb + st * STEP;
+      const int ps = a.page_size;
+      const int pa = t0 / ps;
+      __amdgpu_buffer_rsrc_t ka, va, kb2, vb2;
+      page_views<D>(a, page_ids, e0, g, pa, ke, ka, va);
+      page_views<D>(a, page_ids, e0, g, pa + 1, ke, kb2, vb2);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int p = i * 64 + lane;            // 16-byte chunk index inside the stage
-      const int row = p / CPR;
-      const int cc = p - row * CPR;
-      const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
-      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
-      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      for (int i = 0; i < NDMA; ++i) {
+        const int p = i * 64 + lane;
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const int tok0 = t0 + i * (64 / CPR);
+        const bool second = tok0 / ps != pa;
+        const uint32_t rbase = (uint32_t)(t0 + row - (pa + (second ? 1 : 0)) * ps) * ROW;
+        dma16(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int p = i * 64 + lane;            // 16-byte chunk index inside the stage
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
+        dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      }
     }
   };
 
@@ -625,36 +718,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   if (q == 0 && lse != nullptr) lse[row] = wsum > 0.f ? mx + __logf(wsum) : kNegInf;
 }
 
-template <int D, bool DIRECT>
-static hipError_t launch_decode_d(const DecodeArgs& a, int w, dim3 grid, hipStream_t st) {
+template <int D, bool DIRECT, bool PAGED>
+static void launch_split_d(const DecodeArgs& a, int w, dim3 grid, const int32_t* ids, hipStream_t st) {
   switch (w) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, DIRECT>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT>), grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, DIRECT, PAGED>), grid, dim3(64), 0, st, a, ids); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT, PAGED>), grid, dim3(128), 0, st, a, ids); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT, PAGED>), grid, dim3(256), 0, st, a, ids); break;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
-                               bool direct, hipStream_t stream) {
+template <bool DIRECT, bool PAGED>
+static void launch_decode_mode(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
+                               const int32_t* ids, hipStream_t stream) {
   if (a.chunk_waves > 1) {  // q_len * G <= 16: chunk-wave kernel, one row group
     dim3 grid(a.num_slots, num_kv_heads, batch);
-    if (head_dim == 64) {
-      if (direct) hipLaunchKernelGGL((decode_cw_kernel<64, 4, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((decode_cw_kernel<64, 4, false>), grid, dim3(256), 0, stream, a);
-    } else {
-      if (direct) hipLaunchKernelGGL((decode_cw_kernel<128, 2, true>), grid, dim3(128), 0, stream, a);
-      else hipLaunchKernelGGL((decode_cw_kernel<128, 2, false>), grid, dim3(128), 0, stream, a);
-    }
-    return hipGetLastError();
+    if (head_dim == 64)
+      hipLaunchKernelGGL((decode_cw_kernel<64, 4, DIRECT, PAGED>), grid, dim3(256), 0, stream, a, ids);
+    else
+      hipLaunchKernelGGL((decode_cw_kernel<128, 2, DIRECT, PAGED>), grid, dim3(128), 0, stream, a, ids);
+    return;
   }
   const int w = decode_waves(a.q_len * a.group);
   dim3 grid(a.num_slots, num_kv_heads * a.row_groups, batch);
-  if (head_dim == 64)
-    return direct ? launch_decode_d<64, true>(a, w, grid, stream)
-                  : launch_decode_d<64, false>(a, w, grid, stream);
-  return direct ? launch_decode_d<128, true>(a, w, grid, stream)
-                : launch_decode_d<128, false>(a, w, grid, stream);
+  if (head_dim == 64) launch_split_d<64, DIRECT, PAGED>(a, w, grid, ids, stream);
+  else launch_split_d<128, DIRECT, PAGED>(a, w, grid, ids, stream);
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
+                               bool direct, const int32_t* page_ids, hipStream_t stream) {
+  if (page_ids != nullptr) {
+    if (direct) launch_decode_mode<true, true>(a, head_dim, batch, num_kv_heads, page_ids, stream);
+    else launch_decode_mode<false, true>(a, head_dim, batch, num_kv_heads, page_ids, stream);
+  } else {
+    if (direct) launch_decode_mode<true, false>(a, head_dim, batch, num_kv_heads, nullptr, stream);
+    else launch_decode_mode<false, false>(a, head_dim, batch, num_kv_heads, nullptr, stream);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows, int num_slots,

@@ -47,6 +47,32 @@ struct DecodeArgs {
   float* part_lse;     // [rows, num_slots]
   void* out;           // [rows, D] bf16         (direct mode: one chunk per sequence)
   float* lse;          // [rows]
+  // Paged KV (paged kernels only): k and v are caches [num_pages, Hkv, page_size, D];
+  // sequence b owns page-list entries [kv_page_indptr[b], kv_page_indptr[b+1]) of the
+  // page ids (passed to the kernels separately) and fills its last page up to
+  // kv_last_page_len[b].
+  const int32_t* kv_page_indptr;
+  const int32_t* kv_last_page_len;
+  int64_t num_page_entries;
+  int64_t num_pages;
+  int32_t page_size;   // a multiple of 16
+  int32_t num_kv_heads;
+};
+
+// KV append into a paged cache [num_pages, Hkv, page_size, D] (bf16).
+struct AppendArgs {
+  const void* k_new;             // [total_new, Hkv, D]
+  const void* v_new;
+  const int32_t* append_indptr;  // [B+1] rows of k_new/v_new per sequence
+  const int32_t* kv_page_indptr; // [B+1] (after the append)
+  const int32_t* kv_last_page_len;
+  int64_t total_new;
+  int64_t num_page_entries;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  void* k_cache;
+  void* v_cache;
 };
 
 // Wavefronts per decode workgroup (16 query rows each) for M rows sharing a KV head.
@@ -60,8 +86,12 @@ inline int decode_chunk_waves(int rows, int head_dim) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
                           hipStream_t stream);
+// page_ids: the page list of a paged cache (nullptr for contiguous HND K/V).
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch,
-                               int num_kv_heads, bool direct, hipStream_t stream);
+                               int num_kv_heads, bool direct, const int32_t* page_ids,
+                               hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, int head_dim, int batch, int max_new,
+                            const int32_t* page_ids, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows,
                         int num_slots, int head_dim, void* out, float* lse,
                         hipStream_t stream);

@@ -41,6 +41,19 @@ _SIGS = {
     "sink_attn_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_decode_paged": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,      # q k v sinks
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                       # page table
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,          # b ql ent pages
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,          # ps maxkv hq hkv
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,          # d scale causal ns
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_kv_append": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                       # k_new v_new app
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                       # page table
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,                          # ps hkv d
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "sink_attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sink_attn_last_hip_error": (ctypes.c_int, []),
     "sink_attn_version": (ctypes.c_char_p, []),
@@ -265,3 +278,72 @@ def merge(part_o, part_lse, out=None, lse=None, return_lse: bool = True):
 
 def version() -> str:
     return load().sink_attn_version().decode()
+
+
+def _page_table(kv_page_indptr, kv_page_indices, kv_last_page_len, batch):
+    _dev_tensor(kv_page_indptr, torch.int32, "kv_page_indptr", 1)
+    _dev_tensor(kv_page_indices, torch.int32, "kv_page_indices", 1)
+    _dev_tensor(kv_last_page_len, torch.int32, "kv_last_page_len", 1)
+    _need(kv_page_indptr.numel() == batch + 1, "kv_page_indptr must be [batch+1]")
+    _need(kv_last_page_len.numel() == batch, "kv_last_page_len must be [batch]")
+
+
+def _cache_dims(k_cache, v_cache):
+    _dev_tensor(k_cache, torch.bfloat16, "k_cache", 4)
+    _dev_tensor(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(k_cache.shape == v_cache.shape, "k_cache and v_cache must match")
+    return k_cache.shape  # num_pages, Hkv, page_size, D
+
+
+def decode_paged(q, k_cache, v_cache, sinks, kv_page_indptr, kv_page_indices,
+                 kv_last_page_len, max_kv_len: int, sm_scale: Optional[float] = None,
+                 causal: bool = True, num_splits: int = 0, workspace=None, out=None, lse=None,
+                 return_lse: bool = True):
+    """Decode over a paged cache [num_pages, Hkv, page_size, D] (HND inside a page).
+    q [B, q_len, Hq, D] bf16.  Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq])."""
+    lib = load()
+    _dev_tensor(q, torch.bfloat16, "q", 4)
+    b, ql, hq, d = q.shape
+    num_pages, hkv, ps, dk = _cache_dims(k_cache, v_cache)
+    _need(dk == d, "cache head_dim must match q")
+    _page_table(kv_page_indptr, kv_page_indices, kv_last_page_len, b)
+    sinks = _sinks_arg(sinks, hq, q.device)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if workspace is None:
+        workspace = decode_workspace(b, ql, hq, hkv, d, max_kv_len, num_splits, q.device)
+    else:
+        _dev_tensor(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((b, ql, hq), dtype=torch.float32, device=q.device)
+    rc = lib.sink_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sinks),
+                                    _ptr(kv_page_indptr), _ptr(kv_page_indices),
+                                    _ptr(kv_last_page_len), b, ql, kv_page_indices.numel(),
+                                    num_pages, ps, int(max_kv_len), hq, hkv, d, scale,
+                                    int(bool(causal)), int(num_splits), _ptr(workspace),
+                                    workspace.numel(), _ptr(out), _ptr(lse), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def kv_append(k_new, v_new, append_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
+              k_cache, v_cache, max_append_len: int):
+    """Write k_new/v_new [total_new, Hkv, D] into the paged caches in place (the page table
+    already counts the new tokens)."""
+    lib = load()
+    _dev_tensor(k_new, torch.bfloat16, "k_new", 3)
+    _dev_tensor(v_new, torch.bfloat16, "v_new", 3)
+    _need(k_new.shape == v_new.shape, "k_new and v_new must match")
+    _dev_tensor(append_indptr, torch.int32, "append_indptr", 1)
+    b = append_indptr.numel() - 1
+    num_pages, hkv, ps, d = _cache_dims(k_cache, v_cache)
+    _need(k_new.shape[1] == hkv and k_new.shape[2] == d, "k_new must be [total_new, Hkv, D]")
+    _page_table(kv_page_indptr, kv_page_indices, kv_last_page_len, b)
+    rc = lib.sink_attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(append_indptr),
+                                 _ptr(kv_page_indptr), _ptr(kv_page_indices),
+                                 _ptr(kv_last_page_len), b, int(max_append_len),
+                                 k_new.shape[0], kv_page_indices.numel(), num_pages, ps, hkv, d,
+                                 _ptr(k_cache), _ptr(v_cache), _stream(k_new.device))
+    _check(rc)
+    return k_cache, v_cache

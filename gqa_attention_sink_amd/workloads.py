@@ -182,3 +182,62 @@ def make(name: str, device="cpu", seed: Optional[int] = None, **override) -> Wor
                         device, name)
     w.seed = seed
     return w
+
+
+@dataclass
+class PagedKV:
+    """A paged copy of a workload's K/V: caches [num_pages, Hkv, page_size, D] (HND
+    inside a page) and the page table that maps every sequence's tokens to pages."""
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    kv_page_indptr: torch.Tensor     # int32 [B+1]
+    kv_page_indices: torch.Tensor    # int32 [entries]
+    kv_last_page_len: torch.Tensor   # int32 [B]
+    page_size: int
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_cache.shape[0]
+
+
+def make_paged(w: "Workload", page_size: int, seed: int, spare_pages: int = 7,
+               fill: str = "randn") -> PagedKV:
+    """Scatter a workload's K/V into a paged cache.  Page ids come from a seeded
+    permutation (so a sequence's pages are scattered over the cache) and ``spare_pages``
+    pages belong to no sequence.  Slots no token occupies hold ``fill``: "randn" (bf16
+    draws) or "nan"."""
+    device = w.k.device
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    npages = [-(-lk // page_size) for lk in w.lens_kv]
+    total = sum(npages) + spare_pages
+    perm = torch.randperm(total, generator=gen)
+    hkv, d = w.hkv, w.d
+    if fill == "nan":
+        kc = torch.full((total, hkv, page_size, d), float("nan"), dtype=torch.bfloat16,
+                        device=device)
+        vc = kc.clone()
+    else:
+        g2 = _gen(device, seed + 1)
+        kc = _randn_bf16((total, hkv, page_size, d), g2, device)
+        vc = _randn_bf16((total, hkv, page_size, d), g2, device)
+    indptr, indices, last = [0], [], []
+    tok_page, tok_slot = [], []
+    p = 0
+    for lk, n in zip(w.lens_kv, npages):
+        pages = perm[p:p + n].tolist()
+        p += n
+        indices += pages
+        indptr.append(len(indices))
+        last.append(lk - (n - 1) * page_size if n else 0)
+        for t in range(lk):
+            tok_page.append(pages[t // page_size])
+            tok_slot.append(t % page_size)
+    if tok_page:
+        tp = torch.tensor(tok_page, dtype=torch.long, device=device)
+        ts = torch.tensor(tok_slot, dtype=torch.long, device=device)
+        # [pages, ps, Hkv, D] views of the caches receive the token-major K/V rows
+        kc.permute(0, 2, 1, 3)[tp, ts] = w.k.permute(1, 0, 2)
+        vc.permute(0, 2, 1, 3)[tp, ts] = w.v.permute(1, 0, 2)
+    as_i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=device)  # noqa: E731
+    return PagedKV(kc, vc, as_i32(indptr), as_i32(indices if indices else [0]), as_i32(last),
+                   page_size)

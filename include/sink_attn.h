@@ -154,6 +154,52 @@ int sink_attn_merge(const float* part_o, const float* part_lse, int64_t rows,
                     int32_t num_slots, int32_t head_dim, void* out, float* lse,
                     void* stream);
 
+/*
+ * Paged KV cache.  "Hosting Qwen on Blackwell" (introduction) keeps KV caches head-major
+ * so they can be split or joined by head; "GPT-OSS on day 0" ("Kernels for GPT-OSS")
+ * puts the sink into the attention templates of a paged-KV library.  The page table
+ * follows that library's convention:
+ *
+ *  k_cache, v_cache  bf16 [num_pages, num_kv_heads, page_size, head_dim]: inside a page
+ *                    heads lead and each head's tokens are contiguous (HND per page).
+ *  kv_page_indptr    int32 [batch+1]: sequence b owns entries [indptr[b], indptr[b+1])
+ *                    of kv_page_indices, in token order.
+ *  kv_page_indices   int32 [num_page_entries]: page ids in [0, num_pages).
+ *  kv_last_page_len  int32 [batch]: tokens in the sequence's last page (1..page_size);
+ *                    length L_b = (n_b - 1) * page_size + last_page_len[b], 0 if n_b = 0.
+ *  page_size         a multiple of 16, at most 4096 (a 32-key tile then spans at most
+ *                    two pages).
+ * Device-side values are clamped (page ids to the cache, list offsets to the list), so
+ * a malformed table gives wrong numbers, never a fault.
+ */
+
+/* Decode over a paged cache; every other argument and the workspace are as for
+ * sink_attn_decode (workspace size from sink_attn_decode_workspace_bytes).  max_kv_len
+ * is a host upper bound of L_b. */
+int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                           const float* sinks, const int32_t* kv_page_indptr,
+                           const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                           int32_t batch, int32_t q_len, int64_t num_page_entries,
+                           int64_t num_pages, int32_t page_size, int32_t max_kv_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           float sm_scale, int32_t causal, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Append new keys and values to a paged cache (the step before attention reads them).
+ *  k_new, v_new   bf16 [total_new, num_kv_heads, head_dim], token-major as a projection
+ *                 writes them; sequence b owns rows [append_indptr[b], append_indptr[b+1]).
+ *  The page table already describes the sequences WITH the new tokens: new token i of
+ *  sequence b (of n_b) is written at position L_b - n_b + i.  Rows whose position would
+ *  be negative are skipped.  max_append_len: host upper bound of n_b.
+ */
+int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
+                        const int32_t* kv_page_indptr, const int32_t* kv_page_indices,
+                        const int32_t* kv_last_page_len, int32_t batch, int32_t max_append_len,
+                        int64_t total_new, int64_t num_page_entries, int64_t num_pages,
+                        int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                        void* k_cache, void* v_cache, void* stream);
+
 /* Static text for a status code. */
 const char* sink_attn_status_str(int status);
 

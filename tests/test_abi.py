@@ -164,3 +164,31 @@ def test_python_binding_rejects_cpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         sa.prefill(q, k, k, None, cu, cu, 4)
+
+
+def test_paged_validation(lib):
+    dp = lib.sink_attn_decode_paged
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, ind=FAKE, idx=FAKE, last=FAKE, batch=2,
+                 ql=1, ent=8, pages=8, ps=16, maxk=32, hq=64, hkv=2, d=64, scale=0.125,
+                 causal=1, ns=0, ws=None, wsb=0, out=FAKE, lse=None)
+        a.update(kw)
+        return dp(a["q"], a["k"], a["v"], a["sinks"], a["ind"], a["idx"], a["last"], a["batch"],
+                  a["ql"], a["ent"], a["pages"], a["ps"], a["maxk"], a["hq"], a["hkv"], a["d"],
+                  a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["out"], a["lse"], None)
+    assert call(idx=None) == INVALID and call(last=None) == INVALID and call(ind=None) == INVALID
+    assert call(pages=0) == INVALID and call(ent=-1) == INVALID
+    assert call(ps=8) == UNSUPPORTED and call(ps=24) == UNSUPPORTED and call(ps=8192) == UNSUPPORTED
+    assert call(hq=64, hkv=3) == INVALID and call(d=96) == UNSUPPORTED and call(ql=5) == UNSUPPORTED
+    assert call(ws=None, wsb=0) == WORKSPACE   # 32 rows per KV head: 4 slots need a workspace
+    ap = lib.sink_attn_kv_append
+    def acall(**kw):
+        a = dict(kn=FAKE, vn=FAKE, app=FAKE, ind=FAKE, idx=FAKE, last=FAKE, batch=2, maxn=4,
+                 tot=8, ent=8, pages=8, ps=16, hkv=2, d=64, kc=FAKE, vc=FAKE)
+        a.update(kw)
+        return ap(a["kn"], a["vn"], a["app"], a["ind"], a["idx"], a["last"], a["batch"], a["maxn"],
+                  a["tot"], a["ent"], a["pages"], a["ps"], a["hkv"], a["d"], a["kc"], a["vc"], None)
+    assert acall(kn=None) == INVALID and acall(kc=None) == INVALID and acall(app=None) == INVALID
+    assert acall(batch=0) == INVALID and acall(pages=0) == INVALID and acall(hkv=0) == INVALID
+    assert acall(ps=20) == UNSUPPORTED and acall(d=80) == UNSUPPORTED
+    assert acall(maxn=0) == OK and acall(tot=0) == OK      # nothing to write: no launch

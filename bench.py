@@ -9,7 +9,8 @@ Before every step a 512 MiB read (a sum over a scratch buffer) evicts the 256 MB
 Infinity Cache and the L2s with clean lines, so each step streams its K/V from HBM and
 pays no write-back of dirty lines; only the attention kernels sit inside the timed
 event pair.  The line also reports the other workloads (varlen and long prefill in
-TFLOP/s, speculative decode in GB/s) and the fp64 CPU oracle on a bounded sample.
+TFLOP/s; speculative decode, decode over a paged cache and the paged KV append in
+GB/s) and the fp64 CPU oracle on a bounded sample.
 
 Algorithmic work (implementation overheads such as split partials are not counted):
   decode bytes  = K+V of every visible key once per KV head + Q + out + lse + sinks +
@@ -171,6 +172,62 @@ def bench_prefill(sa, w, steps, warmup, flush):
     return dict(ms=float(np.mean(ms)), ms_min=float(np.min(ms)), wall_s=wall)
 
 
+def time_calls(fn, steps, warmup, flush):
+    """Mean/min milliseconds of fn() between HIP events, each call after a cache flush."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = Timer(steps)
+    for i in range(steps):
+        flush.sum()
+        t.mark(i, 0)
+        fn()
+        t.mark(i, 1)
+    torch.cuda.synchronize()
+    ms = t.ms(0, 1)
+    return float(np.mean(ms)), float(np.min(ms))
+
+
+def bench_paged(sa, steps, warmup, flush):
+    """Decode over a paged cache (the gpt-oss-like batch, page_size 16, pages scattered
+    by a seeded permutation) and the KV append of a mixed-length prefill batch into a
+    paged cache.  Bytes are algorithmic: decode as the contiguous decode plus the page
+    list; append = new K and V read once and written once."""
+    from gqa_attention_sink_amd import workloads as wl
+    res = {}
+    w = wl.make("decode_gptoss", device="cuda")
+    pk = wl.make_paged(w, 16, seed=4242)
+    ws = sa.decode_workspace(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
+    out = torch.empty_like(w.q)
+    lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
+    fn = lambda: sa.decode_paged(w.q, pk.k_cache, pk.v_cache, w.sinks, pk.kv_page_indptr,  # noqa: E731
+                                 pk.kv_page_indices, pk.kv_last_page_len, w.max_kv, w.scale,
+                                 w.causal, w.num_splits, workspace=ws, out=out, lse=lse)
+    ms, ms_min = time_calls(fn, steps, warmup, flush)
+    nbytes = decode_bytes(w) + pk.kv_page_indices.numel() * 4 + w.batch * 4
+    res["paged_decode"] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "ms": round(ms, 4), "ms_min": round(ms_min, 4), "page_size": 16,
+                           "workload": "decode_gptoss in a paged cache", "bytes": nbytes}
+    del w, pk, ws
+    torch.cuda.empty_cache()
+    p = wl.make("varlen_prefill", device="cuda")
+    pk = wl.make_paged(p, 16, seed=4343)
+    k_new = p.k.permute(1, 0, 2).contiguous()
+    v_new = p.v.permute(1, 0, 2).contiguous()
+    app = p.cu_seqlens_kv
+    fn = lambda: sa.kv_append(k_new, v_new, app, pk.kv_page_indptr, pk.kv_page_indices,  # noqa: E731
+                              pk.kv_last_page_len, pk.k_cache, pk.v_cache, p.max_kv)
+    ms, ms_min = time_calls(fn, steps, warmup, flush)
+    nbytes = 2 * 2 * k_new.numel() * 2
+    res["kv_append"] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                        "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "ms": round(ms, 4), "ms_min": round(ms_min, 4), "page_size": 16,
+                        "workload": "varlen_prefill K/V appended to a paged cache",
+                        "tokens": int(k_new.shape[0]), "bytes": nbytes}
+    return res
+
+
 def cpu_baseline(w_gpu, budget_s=20.0):
     """The fp64 oracle on a bounded sample of the decode workload: whole sequences,
     taken in order until about budget_s seconds of CPU work; the rate is scaled to the
@@ -308,6 +365,9 @@ def main():
                                  "split_ms": round(r5["split_ms"], 4),
                                  "merge_ms": round(r5["merge_ms"], 4), "bytes": b5}
         del d5
+        torch.cuda.empty_cache()
+        _say("workload paged decode / kv append")
+        others.update(bench_paged(sa, max(5, args.steps // 2), 2, flush))
         torch.cuda.empty_cache()
         line["others"] = others
     if not args.no_cpu_baseline:

@@ -18,3 +18,8 @@ from .paged_kv import (  # noqa: F401
     kv_append,
     sink_attention_decode_paged,
 )
+from .yarn_rope import (  # noqa: F401
+    yarn_inv_freq,
+    yarn_mscale,
+    apply_rope,
+)

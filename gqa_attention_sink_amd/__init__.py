@@ -5,6 +5,7 @@ as hand-written HIP kernels for MI355X (gfx950) behind a C ABI (include/sink_att
 """
 from .sink_attn import (  # noqa: F401
     LIB_PATH,
+    RopeParams,
     SinkAttnError,
     decode,
     decode_chunks_per_slot,
@@ -17,5 +18,6 @@ from .sink_attn import (  # noqa: F401
     load,
     merge,
     prefill,
+    rope_apply,
     version,
 )

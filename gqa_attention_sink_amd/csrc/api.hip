@@ -97,16 +97,45 @@ sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const fl
   return a;
 }
 
+// YaRN rotary frequencies for the device, in double precision: f_i = theta^(-2i/D); with
+// factor s > 1 the published YaRN interpolation keeps frequencies with at least
+// beta_fast turns over the original context L, divides those with at most beta_slow
+// turns by s, mixes linearly in between, and scales q and k by 0.1 ln s + 1.
+int make_rope(const sink_attn_rope* r, int d, sa::RopeArgs* out) {
+  *out = sa::RopeArgs{};
+  if (r == nullptr) return SINK_ATTN_OK;
+  const bool finite = isfinite(r->theta) && isfinite(r->factor) && isfinite(r->beta_fast) &&
+                      isfinite(r->beta_slow);
+  if (!finite || r->theta <= 1.0f || r->factor <= 0.0f) return SINK_ATTN_ERR_INVALID_ARG;
+  const bool yarn = r->factor > 1.0f;
+  if (yarn && (r->original_max_pos < 1 || !(r->beta_fast > r->beta_slow) || r->beta_slow < 0.f))
+    return SINK_ATTN_ERR_INVALID_ARG;
+  const double two_pi = 6.283185307179586476925;
+  for (int i = 0; i < d / 2; ++i) {
+    double f = pow((double)r->theta, -2.0 * i / d);
+    if (yarn) {
+      const double turns = (double)r->original_max_pos * f / two_pi;
+      double g = (turns - r->beta_slow) / ((double)r->beta_fast - r->beta_slow);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      f = (1.0 - g) * (f / r->factor) + g * f;
+    }
+    out->freq[i] = f;
+  }
+  out->mscale = yarn ? (float)(0.1 * log((double)r->factor) + 1.0) : 1.0f;
+  out->enabled = 1;
+  return SINK_ATTN_OK;
+}
+
 // Split kernel (+ merge when there is more than one slot) for contiguous or paged KV.
 int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_heads,
                int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
-               const int32_t* page_ids, void* workspace, size_t workspace_bytes, void* out,
-               float* lse, void* stream) {
+               const int32_t* page_ids, const sa::RopeArgs& rope, void* workspace,
+               size_t workspace_bytes, void* out, float* lse, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.num_slots == 1) {  // one slot per row: the split kernel writes the result
     a.out = out;
     a.lse = lse;
-    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, page_ids, st);
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, page_ids, rope, st);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   }
@@ -119,7 +148,7 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
   obytes = (obytes + 255) & ~(int64_t)255;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + obytes);
-  hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, page_ids, st);
+  hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, page_ids, rope, st);
   if (e != hipSuccess) return hip_fail(e);
   e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
   if (e != hipSuccess) return hip_fail(e);
@@ -155,7 +184,8 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
                       int32_t max_seqlen_q, int64_t total_q, int64_t total_kv,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                      float sm_scale, int32_t causal, void* out, float* lse, void* stream) {
+                      float sm_scale, int32_t causal, void* out, float* lse,
+                      const sink_attn_rope* rope, void* stream) {
   try {
     if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_kv || !out) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seqlen_q < 0 || total_q < 0 ||
@@ -189,7 +219,9 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
     a.out = out;
     a.lse = lse;
     if (a.n_qtiles > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, (hipStream_t)stream);
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+    hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, ra, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {
@@ -235,7 +267,7 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
                              int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, float sm_scale,
                              int32_t causal, int32_t num_splits, float* part_o,
-                             float* part_lse, void* stream) {
+                             float* part_lse, const sink_attn_rope* rope, void* stream) {
   try {
     int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
@@ -247,7 +279,10 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
                                    num_splits);
     a.part_o = part_o;
     a.part_lse = part_lse;
-    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, nullptr, (hipStream_t)stream);
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, nullptr, ra,
+                                           (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {
@@ -260,7 +295,7 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
                      int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, float sm_scale, int32_t causal, int32_t num_splits,
                      void* workspace, size_t workspace_bytes, void* out, float* lse,
-                     void* stream) {
+                     const sink_attn_rope* rope, void* stream) {
   try {
     int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
@@ -270,8 +305,10 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
     sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
     return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
-                      num_splits, nullptr, workspace, workspace_bytes, out, lse, stream);
+                      num_splits, nullptr, ra, workspace, workspace_bytes, out, lse, stream);
   } catch (...) {
     return SINK_ATTN_ERR_INTERNAL;
   }
@@ -284,7 +321,8 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
                            int64_t num_pages, int32_t page_size, int32_t max_kv_len,
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            float sm_scale, int32_t causal, int32_t num_splits, void* workspace,
-                           size_t workspace_bytes, void* out, float* lse, void* stream) {
+                           size_t workspace_bytes, void* out, float* lse,
+                           const sink_attn_rope* rope, void* stream) {
   try {
     if (!kv_page_indices || !kv_last_page_len) return SINK_ATTN_ERR_INVALID_ARG;
     if (num_page_entries < 0 || num_pages < 1) return SINK_ATTN_ERR_INVALID_ARG;
@@ -302,8 +340,11 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
     a.num_page_entries = num_page_entries;
     a.num_pages = num_pages;
     a.page_size = page_size;
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
     return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
-                      num_splits, kv_page_indices, workspace, workspace_bytes, out, lse, stream);
+                      num_splits, kv_page_indices, ra, workspace, workspace_bytes, out, lse,
+                      stream);
   } catch (...) {
     return SINK_ATTN_ERR_INTERNAL;
   }
@@ -314,7 +355,8 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* app
                         const int32_t* kv_last_page_len, int32_t batch, int32_t max_append_len,
                         int64_t total_new, int64_t num_page_entries, int64_t num_pages,
                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
-                        void* k_cache, void* v_cache, void* stream) {
+                        void* k_cache, void* v_cache, const sink_attn_rope* rope,
+                        void* stream) {
   try {
     if (!k_new || !v_new || !append_indptr || !kv_page_indptr || !kv_page_indices ||
         !kv_last_page_len || !k_cache || !v_cache)
@@ -324,6 +366,8 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* app
       return SINK_ATTN_ERR_INVALID_ARG;
     if (!page_size_ok(page_size) || !dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
     if (max_append_len == 0 || total_new == 0) return SINK_ATTN_OK;
     sa::AppendArgs a{};
     a.k_new = k_new;
@@ -339,7 +383,29 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* app
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     hipError_t e = sa::launch_kv_append(a, head_dim, batch, max_append_len, kv_page_indices,
-                                        (hipStream_t)stream);
+                                        ra, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_rope_apply(void* x, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                         int64_t token_stride, int64_t head_stride, const int32_t* positions,
+                         const sink_attn_rope* rope, void* stream) {
+  try {
+    if (!x || !positions || !rope || num_tokens < 0 || num_heads < 1) return SINK_ATTN_ERR_INVALID_ARG;
+    if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
+    if (token_stride < 0 || head_stride < 0 || (token_stride % 8) != 0 || (head_stride % 8) != 0 ||
+        ((uintptr_t)x & 15u) != 0)
+      return SINK_ATTN_ERR_INVALID_ARG;  // 16-byte vector access
+    if (num_tokens * num_heads * (head_dim / 16) > ((int64_t)1 << 38)) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+    if (num_tokens == 0) return SINK_ATTN_OK;
+    hipError_t e = sa::launch_rope_apply(x, num_tokens, num_heads, head_dim, token_stride,
+                                         head_stride, positions, ra, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {

@@ -96,7 +96,8 @@ __device__ __forceinline__ int dswz(int row) {
 // NST-1 stages ahead of the compute, and every wavefront reads each stage from LDS.
 template <int D, int W, bool DIRECT, bool PAGED>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
-                                                              const int32_t* __restrict__ page_ids) {
+                                                              const int32_t* __restrict__ page_ids,
+                                                              RopeArgs rope) {
   constexpr int KS = D / 32;              // k-steps (32 head dims) of S^T
   constexpr int DPL = D / 16;             // head dims per lane per V row read = O^T d-tiles
   constexpr int ROW = D * 2;              // bytes per K/V row
@@ -202,6 +203,13 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
   for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)((row_t * Hq + row_h) * ROW + (ks * 32 + cg * 8) * 2);
     qop[ks] = as_bf16x8(load16(qr, row_ok ? off : qbytes));
+  }
+  // YaRN rotation of the query row at its position Lk - q_len + t: pair (i, i + D/2)
+  // sits in qop[ks] and qop[ks + KS/2] of the same lane.
+  if (rope.enabled) {
+    const int64_t pos = (int64_t)lk - a.q_len + row_t;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
   }
   // Online-softmax state in log2 units; the sink joins chunk 0 only and is counted by
   // one lane of the four that share a row.
@@ -366,7 +374,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
 // which cuts the partial traffic written during the KV stream and read by the merge.
 template <int D, int CW, bool DIRECT, bool PAGED>
 __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
-                                                            const int32_t* __restrict__ page_ids) {
+                                                            const int32_t* __restrict__ page_ids,
+                                                            RopeArgs rope) {
   constexpr int KS = D / 32;
   constexpr int DPL = D / 16;
   constexpr int ROW = D * 2;
@@ -500,6 +509,11 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qop[ks] = *(const bf16x8*)&q_lds[w][l16 * ROW + (ks * 32 + cg * 8) * 2];
+  if (rope.enabled) {  // YaRN rotation of the query row at position Lk - q_len + t
+    const int64_t pos = (int64_t)lk - a.q_len + row_t;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
+  }
   const float sig = (c == 0 && a.sinks != nullptr && row_ok) ? sink_lds[w][lane] * kLog2e : kNegInf;
   float m = sig;
   float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;
@@ -719,39 +733,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 }
 
 template <int D, bool DIRECT, bool PAGED>
-static void launch_split_d(const DecodeArgs& a, int w, dim3 grid, const int32_t* ids, hipStream_t st) {
+static void launch_split_d(const DecodeArgs& a, int w, dim3 grid, const int32_t* ids,
+                           const RopeArgs& r, hipStream_t st) {
   switch (w) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, DIRECT, PAGED>), grid, dim3(64), 0, st, a, ids); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT, PAGED>), grid, dim3(128), 0, st, a, ids); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT, PAGED>), grid, dim3(256), 0, st, a, ids); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, DIRECT, PAGED>), grid, dim3(64), 0, st, a, ids, r); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, DIRECT, PAGED>), grid, dim3(128), 0, st, a, ids, r); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 4, DIRECT, PAGED>), grid, dim3(256), 0, st, a, ids, r); break;
   }
 }
 
 template <bool DIRECT, bool PAGED>
 static void launch_decode_mode(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
-                               const int32_t* ids, hipStream_t stream) {
+                               const int32_t* ids, const RopeArgs& r, hipStream_t stream) {
   if (a.chunk_waves > 1) {  // q_len * G <= 16: chunk-wave kernel, one row group
     dim3 grid(a.num_slots, num_kv_heads, batch);
     if (head_dim == 64)
-      hipLaunchKernelGGL((decode_cw_kernel<64, 4, DIRECT, PAGED>), grid, dim3(256), 0, stream, a, ids);
+      hipLaunchKernelGGL((decode_cw_kernel<64, 4, DIRECT, PAGED>), grid, dim3(256), 0, stream, a, ids, r);
     else
-      hipLaunchKernelGGL((decode_cw_kernel<128, 2, DIRECT, PAGED>), grid, dim3(128), 0, stream, a, ids);
+      hipLaunchKernelGGL((decode_cw_kernel<128, 2, DIRECT, PAGED>), grid, dim3(128), 0, stream, a, ids, r);
     return;
   }
   const int w = decode_waves(a.q_len * a.group);
   dim3 grid(a.num_slots, num_kv_heads * a.row_groups, batch);
-  if (head_dim == 64) launch_split_d<64, DIRECT, PAGED>(a, w, grid, ids, stream);
-  else launch_split_d<128, DIRECT, PAGED>(a, w, grid, ids, stream);
+  if (head_dim == 64) launch_split_d<64, DIRECT, PAGED>(a, w, grid, ids, r, stream);
+  else launch_split_d<128, DIRECT, PAGED>(a, w, grid, ids, r, stream);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int num_kv_heads,
-                               bool direct, const int32_t* page_ids, hipStream_t stream) {
+                               bool direct, const int32_t* page_ids, const RopeArgs& rope,
+                               hipStream_t stream) {
   if (page_ids != nullptr) {
-    if (direct) launch_decode_mode<true, true>(a, head_dim, batch, num_kv_heads, page_ids, stream);
-    else launch_decode_mode<false, true>(a, head_dim, batch, num_kv_heads, page_ids, stream);
+    if (direct) launch_decode_mode<true, true>(a, head_dim, batch, num_kv_heads, page_ids, rope, stream);
+    else launch_decode_mode<false, true>(a, head_dim, batch, num_kv_heads, page_ids, rope, stream);
   } else {
-    if (direct) launch_decode_mode<true, false>(a, head_dim, batch, num_kv_heads, nullptr, stream);
-    else launch_decode_mode<false, false>(a, head_dim, batch, num_kv_heads, nullptr, stream);
+    if (direct) launch_decode_mode<true, false>(a, head_dim, batch, num_kv_heads, nullptr, rope, stream);
+    else launch_decode_mode<false, false>(a, head_dim, batch, num_kv_heads, nullptr, rope, stream);
   }
   return hipGetLastError();
 }

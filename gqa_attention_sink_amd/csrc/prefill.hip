@@ -53,7 +53,7 @@ __device__ __forceinline__ int kswz(int row) {
 __device__ __forceinline__ int vswz(int row) { return row & 7; }
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs rope) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) unsigned char ring[C::NS][2][C::UB];
 
@@ -128,6 +128,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
       const uint32_t o = (uint32_t)((l32 * Hq + h) * C::ROW + (ks * 16 + cg * 8) * 2);
       qop[ks] = as_bf16x8(load16(qr, o));
     }
+  }
+  // YaRN rotation of query position p0 + l32 at its key-axis position (bottom-right
+  // alignment): pair (i, i + D/2) sits in qop[ks] and qop[ks + KS/2] of the same lane.
+  if (rope.enabled) {
+    const int64_t pos = (int64_t)off + p0 + l32;
+#pragma unroll
+    for (int ks = 0; ks < C::KS / 2; ++ks)
+      rope_rotate8(qop[ks], qop[ks + C::KS / 2], ks * 16 + cg * 8, pos, rope);
   }
 
   // ---- online-softmax state (log2 units), started from the head's sink
@@ -287,12 +295,13 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
     a.lse[orow] = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
+                          const RopeArgs& rope, hipStream_t stream) {
   dim3 grid((unsigned)(num_kv_heads * a.n_hgroups), (unsigned)a.batch, (unsigned)a.n_qtiles);
   if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(512), 0, stream, a, rope);
   else
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(512), 0, stream, a, rope);
   return hipGetLastError();
 }
 

@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "sa_rope.h"
 #include <stdint.h>
 
 namespace sa {
@@ -84,14 +86,20 @@ inline int decode_chunk_waves(int rows, int head_dim) {
   return rows <= 16 ? (head_dim == 64 ? 4 : 2) : 1;
 }
 
+// rope: YaRN rotation of Q (and of new K in the append) at each row's position;
+// rope.enabled == 0 leaves them unrotated.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
-                          hipStream_t stream);
+                          const RopeArgs& rope, hipStream_t stream);
 // page_ids: the page list of a paged cache (nullptr for contiguous HND K/V).
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch,
                                int num_kv_heads, bool direct, const int32_t* page_ids,
-                               hipStream_t stream);
+                               const RopeArgs& rope, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, int head_dim, int batch, int max_new,
-                            const int32_t* page_ids, hipStream_t stream);
+                            const int32_t* page_ids, const RopeArgs& rope, hipStream_t stream);
+// In-place rotation of x: element (t, h, d) at x + t*token_stride + h*head_stride + d.
+hipError_t launch_rope_apply(void* x, int64_t tokens, int heads, int head_dim,
+                             int64_t token_stride, int64_t head_stride,
+                             const int32_t* positions, const RopeArgs& rope, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows,
                         int num_slots, int head_dim, void* out, float* lse,
                         hipStream_t stream);

@@ -1,0 +1,51 @@
+// YaRN rotary position encoding on the device ("GPT-OSS on day 0", model deltas: YaRN
+// position encoding as in DeepSeek-V3; the published YaRN method: rotary embedding with
+// NTK-by-parts frequency interpolation and an attention temperature).  The host fills
+// the per-pair frequencies in double precision; the device forms each angle
+// position * frequency and reduces it modulo 2*pi in double precision, so large
+// positions keep their accuracy, then takes cos/sin in float.  Pairs are half-split:
+// dimension i rotates with dimension i + D/2.
+#pragma once
+
+#include "sa_device.h"
+
+namespace sa {
+
+constexpr int kMaxRopePairs = 64;  // head_dim <= 128
+
+struct RopeArgs {
+  double freq[kMaxRopePairs];  // radians per position of pair i (after YaRN interpolation)
+  float mscale;                // attention temperature factor, applied to q and to k
+  int32_t enabled;             // 0: no rotation
+};
+
+__device__ __forceinline__ void rope_cos_sin(double f, int64_t pos, float& c, float& s) {
+  const double a = (double)pos * f;
+  const double k = __builtin_rint(a * 0.15915494309189533577);  // turns, rounded
+  const double r = __builtin_fma(-k, 6.283185307179586232, a);   // |r| <= pi (+ rounding)
+  sincosf((float)r, &s, &c);
+}
+
+// Rotate eight half-split pairs held as two bf16 vectors: lo = dims [i0, i0+8),
+// hi = dims [i0 + D/2, i0 + D/2 + 8), at one position; results rounded to bf16 (RNE).
+__device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int i0, int64_t pos,
+                                             const RopeArgs& r) {
+  float x[8], y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float c, s;
+    rope_cos_sin(r.freq[i0 + j], pos, c, s);
+    const float a = (float)lo[j], b = (float)hi[j];
+    x[j] = r.mscale * (a * c - b * s);
+    y[j] = r.mscale * (b * c + a * s);
+  }
+  u32x4 xl, yl;
+  xl.x = pack_bf16x2(x[0], x[1]); xl.y = pack_bf16x2(x[2], x[3]);
+  xl.z = pack_bf16x2(x[4], x[5]); xl.w = pack_bf16x2(x[6], x[7]);
+  yl.x = pack_bf16x2(y[0], y[1]); yl.y = pack_bf16x2(y[2], y[3]);
+  yl.z = pack_bf16x2(y[4], y[5]); yl.w = pack_bf16x2(y[6], y[7]);
+  lo = as_bf16x8(xl);
+  hi = as_bf16x8(yl);
+}
+
+}  // namespace sa

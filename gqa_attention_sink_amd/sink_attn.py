@@ -18,7 +18,23 @@ LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
 
 _lib = None
 
-_SIGS = {
+
+class RopeParams(ctypes.Structure):
+    """YaRN rotary parameters (the C struct sink_attn_rope): pairs (i, i + D/2) rotate by
+    pos * f_i with f_i = theta^(-2i/D), interpolated by YaRN when factor > 1."""
+    _fields_ = [("theta", ctypes.c_float), ("factor", ctypes.c_float),
+                ("original_max_pos", ctypes.c_int32), ("beta_fast", ctypes.c_float),
+                ("beta_slow", ctypes.c_float)]
+
+    def __init__(self, theta=10000.0, factor=1.0, original_max_pos=4096, beta_fast=32.0,
+                 beta_slow=1.0):
+        super().__init__(float(theta), float(factor), int(original_max_pos), float(beta_fast),
+                         float(beta_slow))
+
+
+_ROPE_P = ctypes.POINTER(RopeParams)
+
+_SIGS = {  # entry points that take a rope pointer have it just before the stream
     "sink_attn_prefill": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -58,6 +74,22 @@ _SIGS = {
     "sink_attn_last_hip_error": (ctypes.c_int, []),
     "sink_attn_version": (ctypes.c_char_p, []),
 }
+
+
+for _name in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_partial",
+              "sink_attn_decode_paged", "sink_attn_kv_append"):
+    _res, _args = _SIGS[_name]
+    _SIGS[_name] = (_res, _args[:-1] + [_ROPE_P, _args[-1]])
+_SIGS["sink_attn_rope_apply"] = (ctypes.c_int, [
+    ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+    ctypes.c_int64, ctypes.c_void_p, _ROPE_P, ctypes.c_void_p])
+
+
+def _rope_arg(rope):
+    if rope is None:
+        return None
+    _need(isinstance(rope, RopeParams), "rope must be a RopeParams")
+    return ctypes.byref(rope)
 
 
 def load() -> ctypes.CDLL:
@@ -122,7 +154,7 @@ def _sinks_arg(sinks, hq, device):
 
 def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
             sm_scale: Optional[float] = None, causal: bool = True, out=None, lse=None,
-            return_lse: bool = True):
+            return_lse: bool = True, rope: Optional[RopeParams] = None):
     """Variable-length sink attention prefill.
 
     q [total_q, Hq, D] bf16; k, v [Hkv, total_kv, D] bf16 (HND); sinks fp32 [Hq] or
@@ -155,7 +187,7 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     rc = lib.sink_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
                                _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), tq, tk, hq, hkv,
                                d, scale, int(bool(causal)), _ptr(out), _ptr(lse),
-                               _stream(q.device))
+                               _rope_arg(rope), _stream(q.device))
     _check(rc)
     return out, lse
 
@@ -200,7 +232,7 @@ def _decode_common(q, k, v, kv_indptr):
 
 def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
            causal: bool = True, num_splits: int = 0, workspace=None, out=None, lse=None,
-           return_lse: bool = True):
+           return_lse: bool = True, rope: Optional[RopeParams] = None):
     """Split-KV decode with log-sum-exp merge.
 
     q [B, q_len, Hq, D] bf16 (q_len 1..4); k, v [Hkv, total_kv, D] bf16 (HND);
@@ -226,13 +258,14 @@ def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float]
     rc = lib.sink_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(kv_indptr), b, ql,
                               tk, int(max_kv_len), hq, hkv, d, scale, int(bool(causal)),
                               int(num_splits), _ptr(workspace), workspace.numel(), _ptr(out),
-                              _ptr(lse), _stream(q.device))
+                              _ptr(lse), _rope_arg(rope), _stream(q.device))
     _check(rc)
     return out, lse
 
 
 def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
-                   causal: bool = True, num_splits: int = 0, part_o=None, part_lse=None):
+                   causal: bool = True, num_splits: int = 0, part_o=None, part_lse=None,
+                   rope: Optional[RopeParams] = None):
     """First stage of decode alone.  Returns (part_o [B*q_len*Hq, S, D] fp32,
     part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(q_len, Hq, Hkv, D, max_kv_len,
     num_splits); slot j holds plan chunks [j*C, j*C + C), C = decode_chunks_per_slot(...)."""
@@ -253,7 +286,7 @@ def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optiona
     rc = lib.sink_attn_decode_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(kv_indptr),
                                       b, ql, tk, int(max_kv_len), hq, hkv, d, scale,
                                       int(bool(causal)), int(num_splits), _ptr(part_o),
-                                      _ptr(part_lse), _stream(q.device))
+                                      _ptr(part_lse), _rope_arg(rope), _stream(q.device))
     _check(rc)
     return part_o, part_lse
 
@@ -298,7 +331,7 @@ def _cache_dims(k_cache, v_cache):
 def decode_paged(q, k_cache, v_cache, sinks, kv_page_indptr, kv_page_indices,
                  kv_last_page_len, max_kv_len: int, sm_scale: Optional[float] = None,
                  causal: bool = True, num_splits: int = 0, workspace=None, out=None, lse=None,
-                 return_lse: bool = True):
+                 return_lse: bool = True, rope: Optional[RopeParams] = None):
     """Decode over a paged cache [num_pages, Hkv, page_size, D] (HND inside a page).
     q [B, q_len, Hq, D] bf16.  Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq])."""
     lib = load()
@@ -322,13 +355,14 @@ def decode_paged(q, k_cache, v_cache, sinks, kv_page_indptr, kv_page_indices,
                                     _ptr(kv_last_page_len), b, ql, kv_page_indices.numel(),
                                     num_pages, ps, int(max_kv_len), hq, hkv, d, scale,
                                     int(bool(causal)), int(num_splits), _ptr(workspace),
-                                    workspace.numel(), _ptr(out), _ptr(lse), _stream(q.device))
+                                    workspace.numel(), _ptr(out), _ptr(lse), _rope_arg(rope),
+                                    _stream(q.device))
     _check(rc)
     return out, lse
 
 
 def kv_append(k_new, v_new, append_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
-              k_cache, v_cache, max_append_len: int):
+              k_cache, v_cache, max_append_len: int, rope: Optional[RopeParams] = None):
     """Write k_new/v_new [total_new, Hkv, D] into the paged caches in place (the page table
     already counts the new tokens)."""
     lib = load()
@@ -344,6 +378,25 @@ def kv_append(k_new, v_new, append_indptr, kv_page_indptr, kv_page_indices, kv_l
                                  _ptr(kv_page_indptr), _ptr(kv_page_indices),
                                  _ptr(kv_last_page_len), b, int(max_append_len),
                                  k_new.shape[0], kv_page_indices.numel(), num_pages, ps, hkv, d,
-                                 _ptr(k_cache), _ptr(v_cache), _stream(k_new.device))
+                                 _ptr(k_cache), _ptr(v_cache), _rope_arg(rope),
+                                 _stream(k_new.device))
     _check(rc)
     return k_cache, v_cache
+
+
+def rope_apply(x, positions, rope: RopeParams, token_dim: int = 0, head_dim_axis: int = 1):
+    """Rotate a bf16 tensor in place: x has a token axis, a head axis and a last axis of
+    size D (e.g. [total, H, D] with token_dim=0, head_dim_axis=1, or HND keys
+    [Hkv, total, D] with token_dim=1, head_dim_axis=0); token t at positions[t]."""
+    lib = load()
+    _need(isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 3,
+          "x must be a 3-d bf16 GPU tensor")
+    _need(x.stride(-1) == 1, "the last axis of x must be contiguous")
+    _dev_tensor(positions, torch.int32, "positions", 1)
+    tokens, heads, d = x.shape[token_dim], x.shape[head_dim_axis], x.shape[-1]
+    _need(positions.numel() == tokens, "positions must have one entry per token")
+    rc = lib.sink_attn_rope_apply(_ptr(x), tokens, heads, d, x.stride(token_dim),
+                                  x.stride(head_dim_axis), _ptr(positions), _rope_arg(rope),
+                                  _stream(x.device))
+    _check(rc)
+    return x

@@ -53,6 +53,26 @@ typedef enum {
 } sink_attn_status;
 
 /*
+ * YaRN rotary position encoding ("GPT-OSS on day 0", model deltas: YaRN position
+ * encoding as in DeepSeek-V3; the published YaRN method).  Pairs are half-split
+ * (dimension i rotates with i + D/2) by angle pos * f_i, f_i = theta^(-2i/D); with
+ * factor s > 1 frequencies with at least beta_fast turns over original_max_pos keep f_i,
+ * those with at most beta_slow turns become f_i / s, linear in between, and rotated
+ * vectors are scaled by 0.1 ln s + 1.  Angles are formed and reduced in double precision.
+ * Passing NULL where an entry point takes a `const sink_attn_rope*` means no rotation;
+ * invalid parameters (theta <= 1, factor <= 0, non-finite, or for s > 1
+ * original_max_pos < 1 or beta_fast <= beta_slow or beta_slow < 0) give
+ * SINK_ATTN_ERR_INVALID_ARG.
+ */
+typedef struct {
+  float theta;
+  float factor;
+  int32_t original_max_pos;
+  float beta_fast;
+  float beta_slow;
+} sink_attn_rope;
+
+/*
  * Variable-length prefill ("Sink attention": the same sink rule serves prefill).
  *
  *  q             bf16 [total_q, num_q_heads, head_dim], token-major, contiguous.
@@ -67,13 +87,16 @@ typedef enum {
  *  causal        0 or 1.  When 1, each sequence must have Lk >= Lq (documented).
  *  out           bf16 [total_q, num_q_heads, head_dim].
  *  lse           fp32 [total_q, num_q_heads] or NULL.
+ *  rope          NULL, or YaRN parameters: query i of a sequence is rotated at position
+ *                Lk - Lq + i while it is loaded (keys are used as given: rotate them when
+ *                they are written, see sink_attn_kv_append / sink_attn_rope_apply).
  */
 int sink_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                       int32_t batch, int32_t max_seqlen_q, int64_t total_q,
                       int64_t total_kv, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, float sm_scale, int32_t causal, void* out,
-                      float* lse, void* stream);
+                      float* lse, const sink_attn_rope* rope, void* stream);
 
 /*
  * Decode with 1..4 query tokens per sequence (multi-token / speculative decode), split
@@ -97,13 +120,16 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
  *             workspace must be stream-ordered.
  *  out        bf16 [batch, q_len, num_q_heads, head_dim];  lse fp32 [batch, q_len,
  *             num_q_heads] or NULL.
+ *  rope       NULL, or YaRN parameters: query t is rotated at position Lk - q_len + t
+ *             while it is loaded (keys as given).
  */
 int sink_attn_decode(const void* q, const void* k, const void* v, const float* sinks,
                      const int32_t* kv_indptr, int32_t batch, int32_t q_len,
                      int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, float sm_scale,
                      int32_t causal, int32_t num_splits, void* workspace,
-                     size_t workspace_bytes, void* out, float* lse, void* stream);
+                     size_t workspace_bytes, void* out, float* lse,
+                     const sink_attn_rope* rope, void* stream);
 
 /* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
  * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot). */
@@ -137,7 +163,8 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
                              int32_t q_len, int64_t total_kv, int32_t max_kv_len,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                              float sm_scale, int32_t causal, int32_t num_splits,
-                             float* part_o, float* part_lse, void* stream);
+                             float* part_o, float* part_lse, const sink_attn_rope* rope,
+                             void* stream);
 
 /*
  * Log-sum-exp merge of chunk partials ("Sink attention": blocks along the key axis are
@@ -183,7 +210,8 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
                            int64_t num_pages, int32_t page_size, int32_t max_kv_len,
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            float sm_scale, int32_t causal, int32_t num_splits, void* workspace,
-                           size_t workspace_bytes, void* out, float* lse, void* stream);
+                           size_t workspace_bytes, void* out, float* lse,
+                           const sink_attn_rope* rope, void* stream);
 
 /*
  * Append new keys and values to a paged cache (the step before attention reads them).
@@ -192,13 +220,25 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
  *  The page table already describes the sequences WITH the new tokens: new token i of
  *  sequence b (of n_b) is written at position L_b - n_b + i.  Rows whose position would
  *  be negative are skipped.  max_append_len: host upper bound of n_b.
+ *  rope: NULL, or YaRN parameters: each new key is rotated at its position as it is
+ *  written (values are copied unchanged).
  */
 int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
                         const int32_t* kv_page_indptr, const int32_t* kv_page_indices,
                         const int32_t* kv_last_page_len, int32_t batch, int32_t max_append_len,
                         int64_t total_new, int64_t num_page_entries, int64_t num_pages,
                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
-                        void* k_cache, void* v_cache, void* stream);
+                        void* k_cache, void* v_cache, const sink_attn_rope* rope,
+                        void* stream);
+
+/* In-place YaRN rotation of bf16 vectors: element (t, h, d), t < num_tokens,
+ * h < num_heads, d < head_dim, at x + t*token_stride + h*head_stride + d (strides in
+ * elements, multiples of 8; x 16-byte aligned), token t at positions[t] (int32, device).
+ * For example contiguous HND keys [Hkv, total, D] have token_stride D and head_stride
+ * total*D.  rope must not be NULL. */
+int sink_attn_rope_apply(void* x, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                         int64_t token_stride, int64_t head_stride, const int32_t* positions,
+                         const sink_attn_rope* rope, void* stream);
 
 /* Static text for a status code. */
 const char* sink_attn_status_str(int status);

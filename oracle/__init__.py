@@ -22,4 +22,5 @@ from .yarn_rope import (  # noqa: F401
     yarn_inv_freq,
     yarn_mscale,
     apply_rope,
+    bf16_round,
 )

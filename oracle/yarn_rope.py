@@ -18,6 +18,9 @@ DESIGN.md:
   gamma_i f_i;
 * attention temperature: q and k are each multiplied by m = 0.1 ln(s) + 1 (m = 1 for
   s <= 1);
+* rotated vectors are attention inputs and are stored as bfloat16 (as a separate
+  rotation pass would write them): ``bf16_round`` rounds to the nearest bfloat16, ties to
+  even, so a comparison with attention on rotated inputs can take the same rounding;
 * rotation pairs: dimension i with dimension i + D/2 (the "half-split" layout):
   x'_i = m (x_i cos(p f_i') - x_{i+D/2} sin(p f_i')),
   x'_{i+D/2} = m (x_{i+D/2} cos(p f_i') + x_i sin(p f_i')), at integer position p.
@@ -30,7 +33,7 @@ import numpy as np
 
 from .sink_attention import _f64, _i64
 
-__all__ = ["yarn_inv_freq", "yarn_mscale", "apply_rope"]
+__all__ = ["yarn_inv_freq", "yarn_mscale", "apply_rope", "bf16_round"]
 
 
 def yarn_inv_freq(head_dim: int, theta: float, factor: float, original_max_pos: int,
@@ -63,3 +66,11 @@ def apply_rope(x, positions, theta: float, factor: float = 1.0, original_max_pos
     m = yarn_mscale(factor)
     a, b = x[..., : d // 2], x[..., d // 2:]
     return m * np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits), ties to even;
+    returned as float64.  Finite normal inputs only (what the rotation produces)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)   # np.round: half to even

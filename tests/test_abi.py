@@ -56,7 +56,7 @@ def _prefill(lib, **kw):
     a.update(kw)
     return lib.sink_attn_prefill(a["q"], a["k"], a["v"], a["sinks"], a["cq"], a["ck"],
                                  a["batch"], a["maxq"], a["tq"], a["tk"], a["hq"], a["hkv"],
-                                 a["d"], a["scale"], a["causal"], a["out"], a["lse"], None)
+                                 a["d"], a["scale"], a["causal"], a["out"], a["lse"], None, None)
 
 
 def _decode(lib, **kw):
@@ -67,7 +67,7 @@ def _decode(lib, **kw):
     return lib.sink_attn_decode(a["q"], a["k"], a["v"], a["sinks"], a["ind"], a["batch"],
                                 a["ql"], a["tk"], a["maxk"], a["hq"], a["hkv"], a["d"],
                                 a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["out"],
-                                a["lse"], None)
+                                a["lse"], None, None)
 
 
 @pytest.mark.parametrize("kw,rc", [
@@ -100,8 +100,8 @@ def test_decode_validation(lib, kw, rc):
 
 def test_decode_partial_validation(lib):
     f = lib.sink_attn_decode_partial
-    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 1, 64, 32, 8, 2, 64, 0.125, 1, 0, None, FAKE, None) == INVALID
-    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 9, 64, 32, 8, 2, 64, 0.125, 1, 0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 1, 64, 32, 8, 2, 64, 0.125, 1, 0, None, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 9, 64, 32, 8, 2, 64, 0.125, 1, 0, FAKE, FAKE, None, None) == UNSUPPORTED
 
 
 def test_merge_validation(lib):
@@ -175,7 +175,7 @@ def test_paged_validation(lib):
         a.update(kw)
         return dp(a["q"], a["k"], a["v"], a["sinks"], a["ind"], a["idx"], a["last"], a["batch"],
                   a["ql"], a["ent"], a["pages"], a["ps"], a["maxk"], a["hq"], a["hkv"], a["d"],
-                  a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["out"], a["lse"], None)
+                  a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["out"], a["lse"], None, None)
     assert call(idx=None) == INVALID and call(last=None) == INVALID and call(ind=None) == INVALID
     assert call(pages=0) == INVALID and call(ent=-1) == INVALID
     assert call(ps=8) == UNSUPPORTED and call(ps=24) == UNSUPPORTED and call(ps=8192) == UNSUPPORTED
@@ -187,8 +187,33 @@ def test_paged_validation(lib):
                  tot=8, ent=8, pages=8, ps=16, hkv=2, d=64, kc=FAKE, vc=FAKE)
         a.update(kw)
         return ap(a["kn"], a["vn"], a["app"], a["ind"], a["idx"], a["last"], a["batch"], a["maxn"],
-                  a["tot"], a["ent"], a["pages"], a["ps"], a["hkv"], a["d"], a["kc"], a["vc"], None)
+                  a["tot"], a["ent"], a["pages"], a["ps"], a["hkv"], a["d"], a["kc"], a["vc"],
+                  a.get("rope"), None)
     assert acall(kn=None) == INVALID and acall(kc=None) == INVALID and acall(app=None) == INVALID
     assert acall(batch=0) == INVALID and acall(pages=0) == INVALID and acall(hkv=0) == INVALID
     assert acall(ps=20) == UNSUPPORTED and acall(d=80) == UNSUPPORTED
     assert acall(maxn=0) == OK and acall(tot=0) == OK      # nothing to write: no launch
+
+
+def test_rope_validation(lib):
+    R = sa.RopeParams
+    ra = lib.sink_attn_rope_apply
+    ok = R(150000.0, 32.0, 4096, 32.0, 1.0)
+    import ctypes as C
+    def call(rope, **kw):
+        a = dict(x=FAKE, n=4, h=2, d=64, ts=128, hs=64, pos=FAKE)
+        a.update(kw)
+        return ra(a["x"], a["n"], a["h"], a["d"], a["ts"], a["hs"], a["pos"],
+                  None if rope is None else C.byref(rope), None)
+    assert call(None) == INVALID                            # rope required here
+    assert call(R(1.0)) == INVALID and call(R(-5.0)) == INVALID
+    assert call(R(10000.0, 0.0)) == INVALID and call(R(float("nan"))) == INVALID
+    assert call(R(10000.0, 4.0, 0)) == INVALID               # YaRN needs the original length
+    assert call(R(10000.0, 4.0, 4096, 1.0, 1.0)) == INVALID  # beta_fast must exceed beta_slow
+    assert call(ok, d=96) == UNSUPPORTED and call(ok, ts=100) == INVALID
+    assert call(ok, x=C.c_void_p(0x1008)) == INVALID          # 16-byte alignment
+    assert call(ok, n=0) == OK                                # nothing to rotate: no launch
+    # a bad rope on an attention entry point is rejected before any launch
+    bad = C.byref(R(1.0))
+    assert lib.sink_attn_prefill(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 16, 16, 16, 8, 2, 64,
+                                 0.125, 1, FAKE, None, bad, None) == INVALID

@@ -6,7 +6,9 @@ import math
 
 import numpy as np
 
-from oracle import apply_rope, yarn_inv_freq, yarn_mscale
+import torch
+
+from oracle import apply_rope, bf16_round, yarn_inv_freq, yarn_mscale
 
 
 def test_two_dim_rotation_is_textbook():
@@ -65,3 +67,17 @@ def test_interpolation_limits():
     mid = ~fast & ~slow
     assert np.all((f[mid] > base[mid] / s) & (f[mid] < base[mid]))
     assert np.all(np.diff(f) < 0)                          # still strictly decreasing
+
+
+def test_bf16_round_is_round_to_nearest_even():
+    # representable values are fixed points; halfway cases go to the even neighbour
+    assert bf16_round(1.0) == 1.0 and bf16_round(-3.0) == -3.0
+    ulp = 2.0 ** -7                          # spacing of bf16 in [1, 2)
+    assert bf16_round(1.0 + ulp / 2) == 1.0              # tie -> even (1.0)
+    assert bf16_round(1.0 + 1.5 * ulp) == 1.0 + 2 * ulp  # tie -> even (1 + 2 ulp)
+    assert bf16_round(1.0 + 0.51 * ulp) == 1.0 + ulp
+    # agrees with torch's float32 -> bfloat16 conversion (RNE) on float32 inputs
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-3, 4, 100000)).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(bf16_round(x.astype(np.float64)), want)

@@ -172,6 +172,12 @@ def bench_prefill(sa, w, steps, warmup, flush):
     return dict(ms=float(np.mean(ms)), ms_min=float(np.min(ms)), wall_s=wall)
 
 
+# YaRN parameters of the rotated bench lines (a long-context configuration: 32x over a
+# 4096-token original context)
+YARN_BENCH = dict(theta=150000.0, factor=32.0, original_max_pos=4096, beta_fast=32.0,
+                  beta_slow=1.0)
+
+
 def time_calls(fn, steps, warmup, flush):
     """Mean/min milliseconds of fn() between HIP events, each call after a cache flush."""
     for _ in range(warmup):
@@ -209,7 +215,19 @@ def bench_paged(sa, steps, warmup, flush):
                            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "ms": round(ms, 4), "ms_min": round(ms_min, 4), "page_size": 16,
                            "workload": "decode_gptoss in a paged cache", "bytes": nbytes}
-    del w, pk, ws
+    # the same step with the queries rotated (YaRN) as the kernel loads them
+    rope = sa.RopeParams(**YARN_BENCH)
+    fn = lambda: sa.decode_paged(w.q, pk.k_cache, pk.v_cache, w.sinks, pk.kv_page_indptr,  # noqa: E731
+                                 pk.kv_page_indices, pk.kv_last_page_len, w.max_kv, w.scale,
+                                 w.causal, w.num_splits, workspace=ws, out=out, lse=lse,
+                                 rope=rope)
+    ms, ms_min = time_calls(fn, steps, warmup, flush)
+    res["paged_decode_rope"] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                                "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "ms": round(ms, 4), "ms_min": round(ms_min, 4),
+                                "workload": "paged_decode with fused YaRN rotation of q",
+                                "rope": YARN_BENCH}
+    del pk, ws
     torch.cuda.empty_cache()
     p = wl.make("varlen_prefill", device="cuda")
     pk = wl.make_paged(p, 16, seed=4343)
@@ -225,6 +243,13 @@ def bench_paged(sa, steps, warmup, flush):
                         "ms": round(ms, 4), "ms_min": round(ms_min, 4), "page_size": 16,
                         "workload": "varlen_prefill K/V appended to a paged cache",
                         "tokens": int(k_new.shape[0]), "bytes": nbytes}
+    fn = lambda: sa.kv_append(k_new, v_new, app, pk.kv_page_indptr, pk.kv_page_indices,  # noqa: E731
+                              pk.kv_last_page_len, pk.k_cache, pk.v_cache, p.max_kv, rope=rope)
+    ms, ms_min = time_calls(fn, steps, warmup, flush)
+    res["kv_append_rope"] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "ms": round(ms, 4), "ms_min": round(ms_min, 4),
+                             "workload": "kv_append with fused YaRN rotation of the keys"}
     return res
 
 

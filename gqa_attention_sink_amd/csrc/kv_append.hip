@@ -39,6 +39,19 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a,
   const int64_t len = np > 0 ? (int64_t)(np - 1) * ps + min(max(a.kv_last_page_len[b], 1), ps) : 0;
 
   const int tok_begin = blockIdx.x * kAppendTok;
+  // (cos, sin) of every (token, pair) of this workgroup, shared by all KV heads
+  __shared__ float2 cs[kAppendTok][D / 2];
+  if (rope.enabled) {
+    for (int q = threadIdx.x; q < kAppendTok * (D / 2); q += kAppendThreads) {
+      const int tl = q / (D / 2);
+      const int pi = q - tl * (D / 2);
+      const int64_t t = len - n_new + tok_begin + tl;
+      float c = 1.f, sn = 0.f;
+      if (tok_begin + tl < n_new && t >= 0) rope_cos_sin(rope.freq[pi], t, c, sn);
+      cs[tl][pi] = make_float2(c, sn);
+    }
+    __syncthreads();
+  }
   const int pairs = kAppendTok * hkv * HP;
   for (int p = threadIdx.x; p < pairs; p += kAppendThreads) {
     const int tl = p / (hkv * HP);
@@ -60,7 +73,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a,
     const u32x4 v_hi = *(const u32x4*)((const __bf16*)a.v_new + src + D / 2);
     if (rope.enabled) {
       bf16x8 lo = as_bf16x8(k_lo), hi = as_bf16x8(k_hi);
-      rope_rotate8(lo, hi, c * 8, t, rope);
+      rope_rotate8_cs(lo, hi, &cs[tl][c * 8], rope.mscale);
       k_lo = __builtin_bit_cast(u32x4, lo);
       k_hi = __builtin_bit_cast(u32x4, hi);
     }

@@ -18,6 +18,8 @@ from .sink_attn import (  # noqa: F401
     load,
     merge,
     prefill,
+    prefill_num_splits,
+    prefill_workspace_bytes,
     rope_apply,
     version,
 )

@@ -45,8 +45,27 @@ inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
   return sa::decode_chunk_waves(q_len * (hq / hkv), d);
 }
 
+// Key-axis splits of a prefill: num_splits > 0 forces them; 0 splits only when the
+// (head group, sequence, query tile) grid would leave the GPU under-filled (fewer than
+// four 8-wavefront workgroups per CU), keeping at least 8 key units (512 keys) per split.
+constexpr int kPrefillTargetWgs = 4 * 256;
+int heads_per_wg(int group);
+int prefill_splits(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,
+                   int32_t num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int group = hq / hkv;
+  const int hg = heads_per_wg(group);
+  const int64_t qtiles = (max_q + 32 * (8 / hg) - 1) / (32 * (8 / hg));
+  const int64_t base = (int64_t)hkv * (group / hg) * batch * (qtiles > 0 ? qtiles : 1);
+  int64_t s = (kPrefillTargetWgs + base - 1) / base;
+  const int64_t units = (max_kv + 63) / 64;
+  if (s > units / 8) s = units / 8;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : (int)s;
+}
+
 // Query heads per prefill workgroup: the largest divisor of the GQA group size <= 4.
-inline int heads_per_wg(int group) {
+int heads_per_wg(int group) {
   for (int hg = 4; hg >= 1; --hg)
     if (group % hg == 0) return hg;
   return 1;
@@ -180,6 +199,77 @@ int sink_attn_last_hip_error(void) { return g_last_hip_error; }
 
 const char* sink_attn_version(void) { return "0.1.0"; }
 
+static int prefill_common(const void* q, const void* k, const void* v, const float* sinks,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                          int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                          int64_t total_q, int64_t total_kv, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                          int32_t causal, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse,
+                          const sink_attn_rope* rope, void* stream) {
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_kv || !out) return SINK_ATTN_ERR_INVALID_ARG;
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seqlen_q < 0 || total_q < 0 ||
+      total_kv < 0 || max_seqlen_kv < 0)
+    return SINK_ATTN_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return SINK_ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(sm_scale)) return SINK_ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SINK_ATTN_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > kMaxSplits) return SINK_ATTN_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)64 * num_q_heads * head_dim * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
+  if (total_kv * head_dim * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
+  if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+  sa::RopeArgs ra;
+  if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_q == 0 || total_q == 0) return SINK_ATTN_OK;  // nothing to compute
+
+  sa::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sinks = sinks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_kv = cu_seqlens_kv;
+  a.total_q = total_q;
+  a.total_kv = total_kv;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.hg = heads_per_wg(a.group);
+  a.pw = 8 / a.hg;
+  a.n_hgroups = a.group / a.hg;
+  a.n_qtiles = (max_seqlen_q + 32 * a.pw - 1) / (32 * a.pw);
+  a.causal = causal;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  const int S = prefill_splits(batch, max_seqlen_q, max_seqlen_kv, num_q_heads, num_kv_heads,
+                               num_splits);
+  const int units = (max_seqlen_kv + 63) / 64;
+  a.num_splits = S;
+  a.split_units = S > 1 ? (units + S - 1) / S : 0x7fffffff / 64;
+  if ((int64_t)a.n_qtiles * S > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  if (S == 1) {
+    hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, ra, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  }
+  const int64_t rows = total_q * num_q_heads;
+  const size_t need = sink_attn_prefill_workspace_bytes(total_q, num_q_heads, head_dim, S);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SINK_ATTN_ERR_WORKSPACE;
+  int64_t obytes = rows * S * head_dim * 4;
+  obytes = (obytes + 255) & ~(int64_t)255;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + obytes);
+  hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, ra, st);
+  if (e != hipSuccess) return hip_fail(e);
+  e = sa::launch_merge(a.part_o, a.part_lse, rows, S, head_dim, out, lse, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return SINK_ATTN_OK;
+}
+
 int sink_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
                       int32_t max_seqlen_q, int64_t total_q, int64_t total_kv,
@@ -187,43 +277,50 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
                       float sm_scale, int32_t causal, void* out, float* lse,
                       const sink_attn_rope* rope, void* stream) {
   try {
-    if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_kv || !out) return SINK_ATTN_ERR_INVALID_ARG;
-    if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seqlen_q < 0 || total_q < 0 ||
-        total_kv < 0)
-      return SINK_ATTN_ERR_INVALID_ARG;
-    if (num_q_heads % num_kv_heads != 0) return SINK_ATTN_ERR_INVALID_ARG;
-    if (!scale_ok(sm_scale)) return SINK_ATTN_ERR_INVALID_ARG;
-    if (causal != 0 && causal != 1) return SINK_ATTN_ERR_INVALID_ARG;
-    if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
-    if ((int64_t)64 * num_q_heads * head_dim * 2 > kMaxSpanBytes) return SINK_ATTN_ERR_UNSUPPORTED;
-    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    if (max_seqlen_q == 0 || total_q == 0) return SINK_ATTN_OK;  // nothing to compute
+    return prefill_common(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, batch, max_seqlen_q, 0,
+                          total_q, total_kv, num_q_heads, num_kv_heads, head_dim, sm_scale,
+                          causal, 1, nullptr, 0, out, lse, rope, stream);
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
 
-    sa::PrefillArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.sinks = sinks;
-    a.cu_q = cu_seqlens_q;
-    a.cu_kv = cu_seqlens_kv;
-    a.total_kv = total_kv;
-    a.batch = batch;
-    a.num_q_heads = num_q_heads;
-    a.group = num_q_heads / num_kv_heads;
-    a.hg = heads_per_wg(a.group);
-    a.pw = 8 / a.hg;
-    a.n_hgroups = a.group / a.hg;
-    a.n_qtiles = (max_seqlen_q + 32 * a.pw - 1) / (32 * a.pw);
-    a.causal = causal;
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
-    a.out = out;
-    a.lse = lse;
-    if (a.n_qtiles > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    sa::RopeArgs ra;
-    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
-    hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, ra, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e);
-    return SINK_ATTN_OK;
+int32_t sink_attn_prefill_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t num_splits) {
+  if (batch < 1 || max_seqlen_q < 0 || max_seqlen_kv < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 || num_splits < 0 ||
+      num_splits > kMaxSplits)
+    return 0;
+  return prefill_splits(batch, max_seqlen_q, max_seqlen_kv, num_q_heads, num_kv_heads, num_splits);
+}
+
+size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t num_splits) {
+  if (total_q < 0 || num_q_heads < 1 || !dim_ok(head_dim) || num_splits < 1 ||
+      num_splits > kMaxSplits)
+    return 0;
+  if (num_splits == 1) return 0;
+  const int64_t rows = total_q * num_q_heads;
+  int64_t bytes = rows * num_splits * head_dim * 4;
+  bytes = (bytes + 255) & ~(int64_t)255;
+  bytes += rows * num_splits * 4;
+  return (size_t)((bytes + 255) & ~(int64_t)255);
+}
+
+int sink_attn_prefill_split(const void* q, const void* k, const void* v, const float* sinks,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                            int64_t total_q, int64_t total_kv, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                            int32_t causal, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* out, float* lse,
+                            const sink_attn_rope* rope, void* stream) {
+  try {
+    return prefill_common(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, batch, max_seqlen_q,
+                          max_seqlen_kv, total_q, total_kv, num_q_heads, num_kv_heads, head_dim,
+                          sm_scale, causal, num_splits, workspace, workspace_bytes, out, lse,
+                          rope, stream);
   } catch (...) {
     return SINK_ATTN_ERR_INTERNAL;
   }

@@ -2,8 +2,9 @@
 //
 // "GPT-OSS on day 0", "Kernels for GPT-OSS" > "Sink attention": softmax(q.K^T*scale
 // + sink).V with the online (max-subtracted) softmax started from (m, d) = (sink, 1);
-// the whole key range of a row is handled by one wavefront, so the sink is counted
-// exactly once.
+// the whole key range of a row is handled by one wavefront (or, when the key axis is
+// split for parallelism, by one wavefront per split, the sink entering split 0 only and
+// the splits merged by log-sum-exp afterwards), so the sink is counted exactly once.
 //
 // Work unit (one workgroup of 8 wavefronts, two per SIMD): one sequence, 32*pw query
 // positions and hg query heads that share one KV head (GQA), hg*pw = 8.  Each
@@ -72,12 +73,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
   const int g = hgi / a.n_hgroups;
   const int hgrp = hgi - g * a.n_hgroups;
   const int b = blockIdx.y;
-  const int qt = a.n_qtiles - 1 - (int)blockIdx.z;  // heaviest tiles dispatched first
+  const int S = a.num_splits;
+  const int qt = a.n_qtiles - 1 - (int)blockIdx.z / S;  // heaviest tiles dispatched first
+  const int split = (int)blockIdx.z % S;
 
-  const int q0 = a.cu_q[b];
-  const int lq = a.cu_q[b + 1] - q0;
-  const int kv0 = a.cu_kv[b];
-  const int lk = a.cu_kv[b + 1] - kv0;
+  // sequence bounds, clamped to the token axes so that no access leaves the tensors
+  const int q0 = (int)min<int64_t>(max(a.cu_q[b], 0), a.total_q);
+  const int lq = (int)min<int64_t>(max(a.cu_q[b + 1], q0), a.total_q) - q0;
+  const int kv0 = (int)min<int64_t>(max(a.cu_kv[b], 0), a.total_kv);
+  const int lk = (int)min<int64_t>(max(a.cu_kv[b + 1], kv0), a.total_kv) - kv0;
   const int wg_p0 = qt * 32 * a.pw;
   if (wg_p0 >= lq) return;
   const int off = lk - lq;  // bottom-right causal alignment
@@ -90,10 +94,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
 
   int kend_wg = a.causal ? min(lk, wg_p0 + 32 * a.pw + off) : lk;
   kend_wg = max(kend_wg, 0);
-  const int n_wg = (kend_wg + C::UNIT - 1) / C::UNIT;
+  // this split's key units [u0, u1) of the workgroup's causal range (one split: all)
+  const int u0 = split * a.split_units;
+  const int n_wg = min((kend_wg + C::UNIT - 1) / C::UNIT, u0 + a.split_units);
   int kend_w = a.causal ? min(lk, p0 + 32 + off) : lk;
   kend_w = has_rows ? max(kend_w, 0) : 0;
-  const int n_w = (kend_w + C::UNIT - 1) / C::UNIT;
+  const int n_w = min((kend_w + C::UNIT - 1) / C::UNIT, n_wg);
+  const int pos = p0 + l32;
+  const bool split_out = S > 1;
+  if (u0 >= n_wg && split > 0) {  // nothing of this split is visible: an empty partial
+    if (has_rows && pos < lq && cg == 0)
+      a.part_lse[((size_t)(q0 + pos) * Hq + h) * S + split] = kNegInf;
+    return;
+  }
 
   // ---- K/V of this (KV head, sequence) through bounded descriptors: units past the
   // sequence end read zeros and cost no memory traffic.
@@ -139,7 +152,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
   }
 
   // ---- online-softmax state (log2 units), started from the head's sink
-  const float sig = (a.sinks != nullptr && has_rows) ? a.sinks[h] * kLog2e : kNegInf;
+  // the sink enters the first split only ("Sink attention": first block only)
+  const float sig = (a.sinks != nullptr && has_rows && split == 0) ? a.sinks[h] * kLog2e : kNegInf;
   float m = sig;
   float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;  // counted once per row
   f32x16 o[C::DT];
@@ -148,7 +162,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[t][j] = 0.f;
   const float sl2 = a.scale_log2;
-  const int pos = p0 + l32;
   const int lim = a.causal ? min(lk - 1, pos + off) : lk - 1;
 
   // Per-lane part of the transposing V reads: lane p of each 16-lane group supplies
@@ -167,9 +180,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
   }
 
 #pragma unroll
-  for (int u = 0; u < C::PD; ++u) issue(u);
+  for (int i = 0; i < C::PD; ++i) issue(u0 + i);
 
-  for (int u = 0; u < n_wg; ++u) {
+  for (int u = u0; u < n_wg; ++u) {
     // unit u has landed once only the PD-1 units issued after it are pending
     wait_vmcnt<(C::PD - 1) * 2 * C::NDMA>();
     __syncthreads();
@@ -281,6 +294,18 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
   const float dr = half_swap_sum(dsum);
   const float inv = dr > 0.f ? 1.0f / dr : 0.f;
   const size_t orow = (size_t)(q0 + pos) * Hq + h;
+  if (split_out) {  // fp32 partial of this split for the log-sum-exp merge
+    float* pdst = a.part_o + (orow * S + split) * D;
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4*)(pdst + 32 * t + 8 * q4 + 4 * cg) =
+            f32x4{o[t][q4 * 4 + 0] * inv, o[t][q4 * 4 + 1] * inv, o[t][q4 * 4 + 2] * inv,
+                  o[t][q4 * 4 + 3] * inv};
+    if (cg == 0) a.part_lse[orow * S + split] = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
+    return;
+  }
   __bf16* dst = (__bf16*)a.out + orow * D;
 #pragma unroll
   for (int t = 0; t < C::DT; ++t)
@@ -297,7 +322,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,
                           const RopeArgs& rope, hipStream_t stream) {
-  dim3 grid((unsigned)(num_kv_heads * a.n_hgroups), (unsigned)a.batch, (unsigned)a.n_qtiles);
+  dim3 grid((unsigned)(num_kv_heads * a.n_hgroups), (unsigned)a.batch,
+            (unsigned)(a.n_qtiles * a.num_splits));
   if (head_dim == 64)
     hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(512), 0, stream, a, rope);
   else

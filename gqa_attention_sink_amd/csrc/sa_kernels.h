@@ -15,6 +15,7 @@ struct PrefillArgs {
   const float* sinks;
   const int32_t* cu_q;
   const int32_t* cu_kv;
+  int64_t total_q;
   int64_t total_kv;
   int32_t batch;
   int32_t num_q_heads;
@@ -27,6 +28,13 @@ struct PrefillArgs {
   float scale_log2;   // sm_scale * log2(e)
   void* out;
   float* lse;
+  // Split along the key axis (num_splits > 1): split s takes key units
+  // [s*split_units, (s+1)*split_units) and writes a partial into part_o/part_lse
+  // ([total_q*Hq, num_splits, D] and [total_q*Hq, num_splits], fp32) for the merge.
+  int32_t num_splits;
+  int32_t split_units;
+  float* part_o;
+  float* part_lse;
 };
 
 struct DecodeArgs {

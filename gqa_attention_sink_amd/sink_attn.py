@@ -80,6 +80,16 @@ for _name in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_partial
               "sink_attn_decode_paged", "sink_attn_kv_append"):
     _res, _args = _SIGS[_name]
     _SIGS[_name] = (_res, _args[:-1] + [_ROPE_P, _args[-1]])
+_SIGS["sink_attn_prefill_split"] = (ctypes.c_int, [
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,          # q k v sinks
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,            # cu cu b maxq
+    ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,              # maxkv tq tk hq
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,              # hkv d sc causal
+    ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,           # ns ws wsb out
+    ctypes.c_void_p, _ROPE_P, ctypes.c_void_p])
+_SIGS["sink_attn_prefill_num_splits"] = (ctypes.c_int32, [ctypes.c_int32] * 6)
+_SIGS["sink_attn_prefill_workspace_bytes"] = (ctypes.c_size_t, [
+    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32])
 _SIGS["sink_attn_rope_apply"] = (ctypes.c_int, [
     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
     ctypes.c_int64, ctypes.c_void_p, _ROPE_P, ctypes.c_void_p])
@@ -154,11 +164,14 @@ def _sinks_arg(sinks, hq, device):
 
 def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
             sm_scale: Optional[float] = None, causal: bool = True, out=None, lse=None,
-            return_lse: bool = True, rope: Optional[RopeParams] = None):
+            return_lse: bool = True, rope: Optional[RopeParams] = None,
+            num_splits: int = 1, max_seqlen_kv: Optional[int] = None, workspace=None):
     """Variable-length sink attention prefill.
 
     q [total_q, Hq, D] bf16; k, v [Hkv, total_kv, D] bf16 (HND); sinks fp32 [Hq] or
     None; cu_seqlens_q / cu_seqlens_kv int32 [B+1] on the GPU; max_seqlen_q a host int.
+    num_splits != 1 splits the key axis across workgroups (0 = planner; needs
+    max_seqlen_kv, a host bound of the key lengths) and merges the splits.
     Returns (out [total_q, Hq, D] bf16, lse [total_q, Hq] fp32 or None)."""
     lib = load()
     _dev_tensor(q, torch.bfloat16, "q", 3)
@@ -184,12 +197,39 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     elif lse is not None:
         _dev_tensor(lse, torch.float32, "lse", 2)
         _need(tuple(lse.shape) == (tq, hq), "lse must be [total_q, Hq]")
-    rc = lib.sink_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
-                               _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), tq, tk, hq, hkv,
-                               d, scale, int(bool(causal)), _ptr(out), _ptr(lse),
-                               _rope_arg(rope), _stream(q.device))
+    if num_splits == 1:
+        rc = lib.sink_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), tq, tk, hq,
+                                   hkv, d, scale, int(bool(causal)), _ptr(out), _ptr(lse),
+                                   _rope_arg(rope), _stream(q.device))
+        _check(rc)
+        return out, lse
+    _need(max_seqlen_kv is not None, "a key-axis split needs max_seqlen_kv")
+    s_res = prefill_num_splits(batch, max_seqlen_q, max_seqlen_kv, hq, hkv, num_splits)
+    nbytes = prefill_workspace_bytes(tq, hq, d, s_res)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _dev_tensor(workspace, torch.uint8, "workspace")
+    rc = lib.sink_attn_prefill_split(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+                                     _ptr(cu_seqlens_kv), batch, int(max_seqlen_q),
+                                     int(max_seqlen_kv), tq, tk, hq, hkv, d, scale,
+                                     int(bool(causal)), int(num_splits), _ptr(workspace),
+                                     workspace.numel(), _ptr(out), _ptr(lse), _rope_arg(rope),
+                                     _stream(q.device))
     _check(rc)
     return out, lse
+
+
+def prefill_num_splits(batch: int, max_seqlen_q: int, max_seqlen_kv: int, num_q_heads: int,
+                       num_kv_heads: int, num_splits: int = 0) -> int:
+    return int(load().sink_attn_prefill_num_splits(batch, int(max_seqlen_q), int(max_seqlen_kv),
+                                                   num_q_heads, num_kv_heads, int(num_splits)))
+
+
+def prefill_workspace_bytes(total_q: int, num_q_heads: int, head_dim: int, splits: int) -> int:
+    return int(load().sink_attn_prefill_workspace_bytes(int(total_q), num_q_heads, head_dim,
+                                                        int(splits)))
 
 
 def decode_chunks_per_slot(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:

@@ -13,8 +13,9 @@ to bfloat16 (round to nearest even); sinks stay float32.  K and V are head-major
 
 The five named workloads follow the shapes of the pages' workloads: a tiny prefill,
 gpt-oss-like decode (64 query heads over 8 KV heads, head_dim 64), a mixed-length
-prefill, a ~6000-token prefill over 4 KV heads (head_dim 128) and multi-token
-(speculative) decode over 32768 cached tokens.
+prefill, a ~6000-token prefill over 4 KV heads (head_dim 128), multi-token
+(speculative) decode over 32768 cached tokens, and a chunked prefill (a 1024-token chunk
+over a 31744-token cached prefix, the way long inputs are prefilled in pieces).
 """
 from __future__ import annotations
 
@@ -43,6 +44,9 @@ CONFIGS = {
     "spec_decode": dict(kind="decode", batch=256, q_len=4, hq=64, hkv=4, d=128,
                         lens=(32768, 32768), sink=("normal", 0.0, 2.0),
                         scale=1 / math.sqrt(128), causal=True, num_splits=32),
+    # chunked prefill: a 1024-token chunk over a 31744-token cached prefix
+    "chunked_prefill": dict(kind="prefill", batch=1, lens=(1024, 1024), prefix=31744, hq=64,
+                            hkv=8, d=64, sink=("normal", 0.0, 2.0), scale=1 / 8, causal=True),
 }
 _ORDER = list(CONFIGS)
 
@@ -174,7 +178,8 @@ def make(name: str, device="cpu", seed: Optional[int] = None, **override) -> Wor
     seed = seed_of(name) if seed is None else seed
     lens = _lens(cfg["batch"], cfg["lens"], _gen("cpu", seed))
     if cfg["kind"] == "prefill":
-        w = make_prefill(lens, lens, cfg["hq"], cfg["hkv"], cfg["d"], cfg["sink"],
+        lens_kv = [x + cfg.get("prefix", 0) for x in lens]
+        w = make_prefill(lens, lens_kv, cfg["hq"], cfg["hkv"], cfg["d"], cfg["sink"],
                          cfg["scale"], cfg["causal"], seed + 7919, device, name)
     else:
         w = make_decode(lens, cfg["q_len"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["sink"],

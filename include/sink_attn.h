@@ -99,6 +99,42 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
                       float* lse, const sink_attn_rope* rope, void* stream);
 
 /*
+ * Prefill with the key axis split across workgroups ("Sink attention": attention is
+ * parallelised over heads and KV length; the sink enters the first block only; blocks
+ * merge by log-sum-exp).  For chunked prefill over a cached prefix (Lk >> Lq) and other
+ * inputs whose (head group, sequence, query tile) grid leaves the GPU under-filled.
+ * Arguments as for sink_attn_prefill, plus:
+ *  max_seqlen_kv  host upper bound of cu_seqlens_kv[b+1] - cu_seqlens_kv[b].
+ *  num_splits     0 = planner (sink_attn_prefill_num_splits); k in 1..64 = k splits of
+ *                 ceil(ceil(max_seqlen_kv/64)/k) 64-key units each.  One split is
+ *                 exactly sink_attn_prefill.
+ *  workspace      256-byte aligned, at least sink_attn_prefill_workspace_bytes(total_q,
+ *                 num_q_heads, head_dim, S) bytes for the resolved split count S (none when
+ *                 S = 1): fp32 partial outputs [total_q*Hq, S, D] and lse [total_q*Hq, S],
+ *                 merged by the merge kernel into out/lse.  No initialisation needed.
+ */
+int sink_attn_prefill_split(const void* q, const void* k, const void* v, const float* sinks,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                            int64_t total_q, int64_t total_kv, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                            int32_t causal, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* out, float* lse,
+                            const sink_attn_rope* rope, void* stream);
+
+/* Resolved split count of sink_attn_prefill_split (0 if the arguments are invalid): with
+ * num_splits = 0, enough splits for about four workgroups per CU, at most 16, each of at
+ * least 512 keys. */
+int32_t sink_attn_prefill_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t num_splits);
+
+/* Workspace bytes of sink_attn_prefill_split for S resolved splits (0 when S = 1 or the
+ * arguments are invalid). */
+size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t num_splits);
+
+/*
  * Decode with 1..4 query tokens per sequence (multi-token / speculative decode), split
  * along the key axis ("Sink attention": attention parallelised over heads and KV
  * length; the sink enters the first block only) and merged by log-sum-exp.

@@ -217,3 +217,30 @@ def test_rope_validation(lib):
     bad = C.byref(R(1.0))
     assert lib.sink_attn_prefill(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 16, 16, 16, 8, 2, 64,
                                  0.125, 1, FAKE, None, bad, None) == INVALID
+
+
+def test_prefill_split_planner_and_validation(lib):
+    ns = lib.sink_attn_prefill_num_splits
+    # 1024 new tokens over 32768 keys, 64 query heads over 8: 16 head groups (4 heads each)
+    # x 16 query tiles (64 positions) = 256 workgroups -> 4 splits for ~1024
+    assert ns(1, 1024, 32768, 64, 8, 0) == 4
+    assert ns(2, 2048, 32768, 64, 8, 0) == 1          # 1024 workgroups already
+    assert ns(1, 64, 32768, 64, 8, 0) == 16           # tiny grid: capped at 16
+    assert ns(1, 64, 1024, 64, 8, 0) == 2             # at least 512 keys per split
+    assert ns(1, 6000, 6000, 64, 4, 0) == 1           # a full prefill fills the GPU
+    assert ns(1, 64, 100, 64, 8, 0) == 1 and ns(2, 64, 64, 8, 8, 5) == 5
+    assert ns(0, 1, 1, 8, 8, 0) == 0 and ns(1, 1, 1, 8, 3, 0) == 0 and ns(1, 1, 1, 8, 8, 65) == 0
+    wb = lib.sink_attn_prefill_workspace_bytes
+    rows, s, d = 4096 * 64, 4, 64
+    o = (rows * s * d * 4 + 255) // 256 * 256
+    assert wb(4096, 64, 64, 4) == (o + rows * s * 4 + 255) // 256 * 256
+    assert wb(4096, 64, 64, 1) == 0 and wb(4096, 64, 96, 4) == 0
+    f = lib.sink_attn_prefill_split
+    def call(**kw):
+        a = dict(ns=4, ws=None, wsb=0, maxkv=4096, d=64)
+        a.update(kw)
+        return f(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 256, a["maxkv"], 256, 4096, 64, 8, a["d"],
+                 0.125, 1, a["ns"], a["ws"], a["wsb"], FAKE, None, None, None)
+    assert call() == WORKSPACE                       # 4 splits need a workspace
+    assert call(ns=-1) == INVALID and call(ns=65) == INVALID and call(maxkv=-1) == INVALID
+    assert call(d=80) == UNSUPPORTED

@@ -8,8 +8,8 @@ Hkv 8, head_dim 64, KV lengths uniform in [1024, 8192]), with inputs resident in
 Before every step a 512 MiB read (a sum over a scratch buffer) evicts the 256 MB
 Infinity Cache and the L2s with clean lines, so each step streams its K/V from HBM and
 pays no write-back of dirty lines; only the attention kernels sit inside the timed
-event pair.  The line also reports the other workloads (varlen and long prefill in
-TFLOP/s; speculative decode, decode over a paged cache and the paged KV append in
+event pair.  The line also reports the other workloads (varlen, long and chunked prefill
+in TFLOP/s; speculative decode, decode over a paged cache and the paged KV append in
 GB/s) and the fp64 CPU oracle on a bounded sample.
 
 Algorithmic work (implementation overheads such as split partials are not counted):
@@ -148,15 +148,21 @@ def bench_decode(sa, w, steps, warmup, flush):
                 wall_s=wall, slots=s)
 
 
-def bench_prefill(sa, w, steps, warmup, flush):
+def bench_prefill(sa, w, steps, warmup, flush, num_splits=1):
     out = torch.empty_like(w.q)
     lse = torch.empty((w.q.shape[0], w.hq), dtype=torch.float32, device="cuda")
+    ws = None
+    if num_splits != 1:
+        ns = sa.prefill_num_splits(w.batch, w.max_q, w.max_kv, w.hq, w.hkv, num_splits)
+        ws = torch.empty(max(256, sa.prefill_workspace_bytes(w.q.shape[0], w.hq, w.d, ns)),
+                         dtype=torch.uint8, device="cuda")
 
     def step(t=None, i=0):
         flush.sum()
         if t: t.mark(i, 0)
         sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q, w.scale,
-                   w.causal, out=out, lse=lse)
+                   w.causal, out=out, lse=lse, num_splits=num_splits, max_seqlen_kv=w.max_kv,
+                   workspace=ws)
         if t: t.mark(i, 1)
 
     for _ in range(warmup):
@@ -379,6 +385,20 @@ def main():
                             "flops": fl}
             del p
             torch.cuda.empty_cache()
+        _say("workload chunked_prefill")
+        p = wl.make("chunked_prefill", device="cuda")
+        fl = prefill_flops(p)
+        ns = sa.prefill_num_splits(p.batch, p.max_q, p.max_kv, p.hq, p.hkv, 0)
+        rs = bench_prefill(sa, p, args.steps, args.warmup, flush, num_splits=0)
+        r1 = bench_prefill(sa, p, args.steps, args.warmup, flush, num_splits=1)
+        tf = fl / (rs["ms"] * 1e-3) / 1e12
+        others["chunked_prefill"] = {
+            "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "ms": round(rs["ms"], 4), "ms_min": round(rs["ms_min"], 4), "flops": fl,
+            "key_splits": ns, "unsplit_TFLOP/s": round(fl / (r1["ms"] * 1e-3) / 1e12, 2),
+            "workload": "1024 new tokens over a 31744-token cached prefix"}
+        del p
+        torch.cuda.empty_cache()
         _say("workload spec_decode")
         d5 = wl.make("spec_decode", device="cuda")
         r5 = bench_decode(sa, d5, max(5, args.steps // 2), 2, flush)

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
   for (int st = 0; st < nsteps; ++st) {
     // stage st has landed once only the NST-2 stages issued after it are pending
     wait_vmcnt<((NST - 2) * 2 * NDMA < 63 ? (NST - 2) * 2 * NDMA : 63)>();
-    __syncthreads();
+    stage_barrier();
     issue(st + NST - 1);  // refills the slot every wavefront finished with (st-1)
 
     const unsigned char* kbuf = ring[st % NST][0];

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
   for (int u = u0; u < n_wg; ++u) {
     // unit u has landed once only the PD-1 units issued after it are pending
     wait_vmcnt<(C::PD - 1) * 2 * C::NDMA>();
-    __syncthreads();
+    stage_barrier();
     issue(u + C::PD);  // refills the slot of unit u-1, which every wavefront finished
     if (u < n_w) {
       const unsigned char* kbuf = ring[u % C::NS][0];

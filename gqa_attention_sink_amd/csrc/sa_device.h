@@ -63,6 +63,14 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, voi
       r, (__attribute__((address_space(3))) void*)lds_wave_base, 4, off, 0, 0, 0);
 }
 
+// Workgroup barrier for the streaming loops, without the memory-model fences that
+// __syncthreads() adds: the release fence would wait for every outstanding vector-memory
+// operation, including the asynchronous LDS copies issued stages ahead, and so drain
+// the ring at every stage.  Callers wait for the copies they need (wait_vmcnt) and their
+// LDS reads are consumed before the barrier; the memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Wait until at most N vector-memory operations of this wavefront are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

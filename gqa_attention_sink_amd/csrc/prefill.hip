@@ -49,9 +49,18 @@ __device__ __forceinline__ int kswz(int row) {
   else return (row >> 1) & 7;
 }
 
-// XOR swizzle of 16-byte chunks inside a V row: the 8 rows touched by one transposing
-// read land in distinct banks.
-__device__ __forceinline__ int vswz(int row) { return row & 7; }
+// XOR swizzle of 16-byte chunks inside a V row for the transposing reads.  The LDS
+// serves 256 bytes (64 banks) per cycle, i.e. 32 lanes of an 8-byte read; those 32 lanes
+// read four consecutive rows (4*cg .. +3, plus a multiple of 8) at four consecutive
+// 16-byte chunks 4t .. 4t+3.  D=128 (one row per 256 bytes): XOR by 4*(row%4) spreads
+// the four rows over disjoint chunk quads.  D=64 (two rows per 256 bytes, rows of equal
+// parity sharing banks): XOR by 4 on rows 2 and 3 separates row 0 from 2 and 1 from 3.
+// (A swizzle by row%8 left 2-way (D=64) and 4-way (D=128) bank conflicts.)
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) return (row & 3) << 2;
+  else return (row & 2) << 1;
+}
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs rope) {
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
       const int cc = p - row * C::CPR;
       const uint32_t rb = (uint32_t)(u * C::UNIT + row) * C::ROW;
       dma16(kr, rb + (uint32_t)((cc ^ kswz<D>(row)) * 16), kbuf + blk * 1024);
-      dma16(vr, rb + (uint32_t)((cc ^ vswz(row)) * 16), vbuf + blk * 1024);
+      dma16(vr, rb + (uint32_t)((cc ^ vswz<D>(row)) * 16), vbuf + blk * 1024);
     }
   };
 
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
 #pragma unroll
     for (int t = 0; t < C::DT; ++t) {
       const int d = 32 * t + dsub;
-      v_lane_off[t] = (uint32_t)(lrow * C::ROW + (((d >> 3) ^ vswz(lrow)) * 16) + (d & 7) * 2);
+      v_lane_off[t] = (uint32_t)(lrow * C::ROW + (((d >> 3) ^ vswz<D>(lrow)) * 16) + (d & 7) * 2);
     }
   }
 

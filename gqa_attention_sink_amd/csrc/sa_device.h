@@ -53,6 +53,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, vo
       r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
 }
 
+// The same bounded view as four descriptor words in scalar registers (base address,
+// stride 0, size in bytes, raw-buffer word 3), for the assembly copy below.
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu;
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = (uint32_t)kBufferWord3;
+  return r;
+}
+
+// dma16 written as assembly: the compiler does not see that the copy writes LDS, so it
+// attaches no wait for it to later LDS reads.  Callers order every LDS read of the
+// copied bytes after their own wait_vmcnt and a workgroup barrier.  lds_base must be
+// wave-uniform.
+__device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 // An offset no bounded view reaches (views are < 2^31 bytes): the copy reads nothing
 // and writes zeros.
 constexpr uint32_t kNoRead = 0x80000000u;
@@ -135,6 +158,15 @@ __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr, const int off) 
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(off) : "memory");
   return r;
+}
+// The same read through the compiler builtin, from a pointer into a __shared__ object
+// (so that the compiler knows which object it reads): the compiler sees the load and
+// places the wait before the first use itself.
+__device__ __forceinline__ u32x2 ds_read_tr16_c(const void* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(void*)p);
+  return __builtin_bit_cast(u32x2, r);
 }
 // Wait for all outstanding LDS reads; ties the given registers to the wait.
 __device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {

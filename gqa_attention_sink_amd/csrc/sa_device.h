@@ -70,10 +70,11 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t byte
 // copied bytes after their own wait_vmcnt and a workgroup barrier.  lds_base must be
 // wave-uniform.
 __device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  // the LDS destination goes through M0, which the compiler loads for the statement
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(off), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
+               : "v"(off), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
 }
 
 // An offset no bounded view reaches (views are < 2^31 bytes): the copy reads nothing

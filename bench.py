@@ -117,13 +117,23 @@ def bench_decode(sa, w, steps, warmup, flush):
                   w.num_splits, workspace=ws, out=out, lse=lse)
         if t: t.mark(i, 1)
 
+    stream = (sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, w.k.shape[1], w.max_kv)
+              if w.num_splits == 0 else None)
+
     def step_split(t, i):
         flush.sum()
         t.mark(i, 0)
-        sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
-                          w.causal, w.num_splits, part_o=po, part_lse=pl)
-        t.mark(i, 1)
-        sa.merge(po, pl, out=out.view(rows, w.d), lse=lse.view(rows))
+        if stream is not None:  # the stream plan's two kernels, as decode runs them
+            sa.decode_stream_partial(w.q, w.k, w.v, w.cu_seqlens_kv, w.max_kv, w.scale,
+                                     w.causal, workspace=ws)
+            t.mark(i, 1)
+            sa.decode_stream_merge(w.sinks, w.cu_seqlens_kv, tuple(w.q.shape), w.k.shape[1],
+                                   w.hkv, w.max_kv, ws, out=out, lse=lse)
+        else:
+            sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                              w.causal, w.num_splits, part_o=po, part_lse=pl)
+            t.mark(i, 1)
+            sa.merge(po, pl, out=out.view(rows, w.d), lse=lse.view(rows))
         t.mark(i, 2)
 
     for _ in range(warmup):
@@ -145,7 +155,10 @@ def bench_decode(sa, w, steps, warmup, flush):
     merge_ms = t2.ms(1, 2)
     return dict(full_ms=float(np.mean(full_ms)), full_ms_min=float(np.min(full_ms)),
                 split_ms=float(np.mean(split_ms)), merge_ms=float(np.mean(merge_ms)),
-                wall_s=wall, slots=s)
+                wall_s=wall, slots=stream[2] if stream is not None else s,
+                plan=("stream" if stream is not None else "chunks"),
+                stream_plan=(dict(range_tokens=stream[0], ranges_per_head=stream[1],
+                                  slots=stream[2]) if stream is not None else None))
 
 
 def bench_prefill(sa, w, steps, warmup, flush, num_splits=1):
@@ -339,9 +352,14 @@ def main():
     split_bytes = decode_bytes(w, split_only=True)
     value = nbytes / (r["full_ms"] * 1e-3) / 1e9
     split_gbs = split_bytes / (r["split_ms"] * 1e-3) / 1e9
-    # the dominant kernel: chunk-wave kernel when a workgroup merges several chunks
-    kname = ("decode_cw_kernel" if sa.decode_chunks_per_slot(w.q_len, w.hq, w.hkv, w.d) > 1
-             else "decode_split_kernel")
+    # the dominant kernel: the stream kernel under the stream plan, else the chunk-wave
+    # kernel when a workgroup merges several chunks, else the split kernel
+    if r["plan"] == "stream":
+        kname = "decode_stream_kernel"
+    elif sa.decode_chunks_per_slot(w.q_len, w.hq, w.hkv, w.d) > 1:
+        kname = "decode_cw_kernel"
+    else:
+        kname = "decode_split_kernel"
     line = {
         "metric": "sink-attn decode HBM GB/s (and prefill TFLOP/s) on 1 MI355X, % of peak",
         "value": round(value, 2),
@@ -357,7 +375,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "sum_kv": sum(w.lens_kv),
-                   "num_splits": w.num_splits, "slots": r["slots"], "seed": w.seed,
+                   "num_splits": w.num_splits, "plan": r["plan"], "slots": r["slots"],
+                   "stream_plan": r["stream_plan"], "seed": w.seed,
                    "parallelism": "single-gpu"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_min": round(r["full_ms_min"], 4),

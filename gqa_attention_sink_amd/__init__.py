@@ -12,6 +12,9 @@ from .sink_attn import (  # noqa: F401
     decode_num_slots,
     decode_paged,
     decode_partial,
+    decode_stream_merge,
+    decode_stream_partial,
+    decode_stream_plan,
     decode_workspace,
     decode_workspace_bytes,
     kv_append,

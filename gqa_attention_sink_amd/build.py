@@ -13,7 +13,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "kv_append.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "decode_stream.hip", "kv_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -45,6 +45,39 @@ inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
   return sa::decode_chunk_waves(q_len * (hq / hkv), d);
 }
 
+// Stream decode plan (contiguous K/V, at most 16 query rows per KV head, planner mode,
+// more than one partial per row): about 4 wavefronts per CU, each taking R tokens of one
+// KV head's token axis; R is at least max_kv/16 (so a sequence overlaps at most 17
+// ranges, the slots a row needs) and a multiple of 32.
+using sa::kStreamMaxSlots;
+constexpr int kStreamWavesTotal = 4 * 256;
+inline bool stream_eligible(int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
+                            int32_t max_kv_len, int32_t num_splits) {
+  return num_splits == 0 && q_len * (hq / hkv) <= 16 &&
+         planned_slots(max_kv_len, num_splits, chunk_waves(q_len, hq, hkv, d)) > 1;
+}
+inline int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
+sa::StreamPlan stream_plan(int32_t batch, int32_t hkv, int64_t total_kv, int32_t max_kv_len) {
+  sa::StreamPlan p{};
+  p.nph = kStreamWavesTotal / hkv > 0 ? kStreamWavesTotal / hkv : 1;
+  int64_t r = round32((total_kv + p.nph - 1) / p.nph);
+  const int64_t r_floor = round32((max_kv_len + kStreamMaxSlots - 2) / (kStreamMaxSlots - 1));
+  if (r < r_floor) r = r_floor;
+  if (r < 32) r = 32;
+  p.R = (int32_t)r;
+  const int64_t sm = (max_kv_len + r - 1) / r + 1;
+  p.smax = (int32_t)(sm < kStreamMaxSlots ? sm : kStreamMaxSlots);
+  p.batch = batch;
+  p.num_kv_heads = hkv;
+  return p;
+}
+inline size_t partial_bytes(int64_t rows, int64_t slots, int d) {
+  int64_t bytes = rows * slots * d * 4;   // partial outputs
+  bytes = (bytes + 255) & ~(int64_t)255;
+  bytes += rows * slots * 4;              // partial lse
+  return (size_t)((bytes + 255) & ~(int64_t)255);
+}
+
 // Key-axis splits of a prefill: num_splits > 0 forces them; 0 splits only when the
 // (head group, sequence, query tile) grid would leave the GPU under-filled (fewer than
 // four 8-wavefront workgroups per CU), keeping at least 8 key units (512 keys) per split.
@@ -151,6 +184,24 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
                const int32_t* page_ids, const sa::RopeArgs& rope, void* workspace,
                size_t workspace_bytes, void* out, float* lse, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (page_ids == nullptr && a.total_kv <= INT32_MAX &&
+      stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits)) {
+    const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
+                                                         head_dim, max_kv_len, num_splits);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+      return SINK_ATTN_ERR_WORKSPACE;
+    const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, a.total_kv, max_kv_len);
+    const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = sa::launch_decode_stream(a, head_dim, sp, rope, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = sa::launch_merge_stream(a, head_dim, sp, rows, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  }
   if (a.num_slots == 1) {  // one slot per row: the split kernel writes the result
     a.out = out;
     a.lse = lse;
@@ -353,10 +404,13 @@ size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t nu
                                                max_kv_len, num_splits);
   if (S == 0) return 0;
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
-  int64_t bytes = rows * S * head_dim * 4;   // partial outputs
-  bytes = (bytes + 255) & ~(int64_t)255;
-  bytes += rows * S * 4;                     // partial lse
-  return (size_t)((bytes + 255) & ~(int64_t)255);
+  // the stream plan (contiguous caches) needs up to kStreamMaxSlots slots per row
+  const int64_t slots =
+      stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits) &&
+              S < kStreamMaxSlots
+          ? kStreamMaxSlots
+          : S;
+  return partial_bytes(rows, slots, head_dim);
 }
 
 int sink_attn_decode_partial(const void* q, const void* k, const void* v, const float* sinks,
@@ -382,6 +436,85 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
                                            (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
+                                     int32_t max_kv_len, int32_t* range_tokens,
+                                     int32_t* ranges_per_head, int32_t* slots) {
+  if (batch < 1 || !slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || total_kv < 0 ||
+      total_kv > INT32_MAX || max_kv_len < 0 ||
+      !stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0))
+    return 0;
+  const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, total_kv, max_kv_len);
+  if (range_tokens) *range_tokens = sp.R;
+  if (ranges_per_head) *ranges_per_head = sp.nph;
+  if (slots) *slots = sp.smax;
+  return 1;
+}
+
+// The two steps of the stream plan on their own (sink_attn_decode runs both).
+static int stream_step(bool partial, const void* q, const void* k, const void* v,
+                       const float* sinks, const int32_t* kv_indptr, int32_t batch,
+                       int32_t q_len, int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, float sm_scale, int32_t causal,
+                       void* workspace, size_t workspace_bytes, void* out, float* lse,
+                       const sink_attn_rope* rope, void* stream) {
+  int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len, num_q_heads,
+                             num_kv_heads, head_dim, sm_scale, causal, 0);
+  if (rc != SINK_ATTN_OK) return rc;
+  if (total_kv > INT32_MAX ||
+      !stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0))
+    return SINK_ATTN_ERR_UNSUPPORTED;
+  if (!partial && !out) return SINK_ATTN_ERR_INVALID_ARG;
+  const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
+                                                       head_dim, max_kv_len, 0);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SINK_ATTN_ERR_WORKSPACE;
+  sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+                                 num_q_heads, num_kv_heads, head_dim, sm_scale, causal, 0);
+  sa::RopeArgs ra;
+  if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+  const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, total_kv, max_kv_len);
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = partial ? sa::launch_decode_stream(a, head_dim, sp, ra, (hipStream_t)stream)
+                         : sa::launch_merge_stream(a, head_dim, sp, rows, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_decode_stream_partial(const void* q, const void* k, const void* v,
+                                    const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                                    int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                    int32_t causal, void* workspace, size_t workspace_bytes,
+                                    const sink_attn_rope* rope, void* stream) {
+  try {
+    return stream_step(true, q, k, v, nullptr, kv_indptr, batch, q_len, total_kv, max_kv_len,
+                       num_q_heads, num_kv_heads, head_dim, sm_scale, causal, workspace,
+                       workspace_bytes, nullptr, nullptr, rope, stream);
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+int sink_attn_decode_stream_merge(const float* sinks, const int32_t* kv_indptr, int32_t batch,
+                                  int32_t q_len, int64_t total_kv, int32_t max_kv_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  const void* workspace, size_t workspace_bytes, void* out,
+                                  float* lse, void* stream) {
+  try {
+    // q, k and v are not read by the merge; the workspace stands in for the checks
+    return stream_step(false, workspace, workspace, workspace, sinks, kv_indptr, batch, q_len,
+                       total_kv, max_kv_len, num_q_heads, num_kv_heads, head_dim, 1.0f, 1,
+                       (void*)workspace, workspace_bytes, out, lse, nullptr, stream);
   } catch (...) {
     return SINK_ATTN_ERR_INTERNAL;
   }

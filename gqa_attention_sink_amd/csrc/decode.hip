@@ -15,8 +15,7 @@
 // O^T = V^T . P^T, so probabilities never leave registers and the per-row softmax
 // state (m, d, rescale) is lane-local.  K and V stream from HBM through
 // an LDS ring with asynchronous buffer->LDS copies; V is transposed in registers.
-#include "sa_device.h"
-#include "sa_kernels.h"
+#include "sa_decode.h"
 
 
 namespace sa {
@@ -29,14 +28,6 @@ __device__ __forceinline__ int plan_chunks(int lk, int num_splits, int cw) {
   if (num_splits > 0) return num_splits;
   const int n = (((lk + 255) >> 8) + cw - 1) / cw * cw;
   return min(16, max(4, n));
-}
-// Sequence b's token range, clamped to the token axis so that no copy can leave K or V
-// even when the index array is malformed.
-__device__ __forceinline__ int seq_begin(const DecodeArgs& a, int b) {
-  return (int)min<int64_t>(max(a.kv_indptr[b], 0), a.total_kv);
-}
-__device__ __forceinline__ int seq_end(const DecodeArgs& a, int b) {
-  return (int)min<int64_t>(max(a.kv_indptr[b + 1], seq_begin(a, b)), a.total_kv);
 }
 // Paged sequence b: its first page-list entry and its length, clamped so that every
 // page-list read stays inside the list.
@@ -76,19 +67,7 @@ __device__ __forceinline__ int chunk_len(int lk, int n) {
   return (cl + 31) & ~31;
 }
 
-// Key of slot i (0..7) in the 32-key step for k-group cg: the S^T accumulator of key
-// tile kt holds keys kt*16 + 4*cg + j (j = 0..3) for the lane's row.
-__device__ __forceinline__ int slot_key(int cg, int i) {
-  return (i < 4) ? (4 * cg + i) : (16 + 4 * cg + (i - 4));
-}
 
-// XOR swizzle of 16-byte chunks inside a K row in LDS: the 16 rows read by one MFMA
-// operand load land in distinct banks.
-template <int D>
-__device__ __forceinline__ int dswz(int row) {
-  if constexpr (D == 128) return row & 15;
-  else return (row >> 1) & 7;
-}
 
 // Decode split kernel.  Workgroup = W wavefronts = one (sequence, KV head, row group,
 // chunk); wavefront w owns 16 query rows.  The chunk's K and V stream from HBM into an
@@ -268,8 +247,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
     // more than 2^8 (exact: numerator and denominator share the stale max)
     float mx = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
                      fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
-    mx = wave_xor_max(mx, 16);
-    mx = wave_xor_max(mx, 32);
+    mx = max_over_16_32(mx);
     const float mxs = mx * sl2;
     if (__any(mxs > m + 8.0f)) {
       const float mnew = fmaxf(m, mxs);
@@ -560,8 +538,7 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
     }
     float mx = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
                      fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
-    mx = wave_xor_max(mx, 16);
-    mx = wave_xor_max(mx, 32);
+    mx = max_over_16_32(mx);
     const float mxs = mx * sl2;
     if (__any(mxs > m + 8.0f)) {
       const float mnew = fmaxf(m, mxs);

@@ -131,6 +131,20 @@ __device__ __forceinline__ float half_swap_sum(float v) { return v + __shfl_xor(
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max over the four lanes l, l^16, l^32, l^48 with the lane-swap instructions (VALU, no
+// LDS round trip): with both operands holding v, v_permlane16_swap leaves the values of
+// the even and of the odd 16-lane rows in the two registers (each in both rows of a
+// pair), and v_permlane32_swap does the same for the two halves.  The s_nop covers the
+// wait a swap needs after a VALU write of its operands.
+__device__ __forceinline__ float max_over_16_32(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  float m = fmaxf(a, b);
+  float c = m, e = m;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(e));
+  return fmaxf(c, e);
+}
+
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -85,6 +85,18 @@ struct AppendArgs {
   void* v_cache;
 };
 
+// Stream decode plan: the token axis of each KV head is cut into ranges of R tokens (a
+// multiple of 32), nph ranges per head, one wavefront each; a row's partials occupy
+// smax slots ([rows, smax, D] outputs then [rows, smax] lse).
+constexpr int kStreamMaxSlots = 17;  // partial slots a row can need under the stream plan
+struct StreamPlan {
+  int32_t R;
+  int32_t nph;
+  int32_t smax;
+  int32_t batch;
+  int32_t num_kv_heads;
+};
+
 // Wavefronts per decode workgroup (16 query rows each) for M rows sharing a KV head.
 inline int decode_waves(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
@@ -108,6 +120,12 @@ hipError_t launch_kv_append(const AppendArgs& a, int head_dim, int batch, int ma
 hipError_t launch_rope_apply(void* x, int64_t tokens, int heads, int head_dim,
                              int64_t token_stride, int64_t head_stride,
                              const int32_t* positions, const RopeArgs& rope, hipStream_t stream);
+// Stream decode (contiguous K/V, q_len * G <= 16): partials into a.part_o / a.part_lse,
+// then their merge with the sinks into a.out / a.lse.
+hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
+                                const RopeArgs& rope, hipStream_t stream);
+hipError_t launch_merge_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
+                               int64_t rows, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows,
                         int num_slots, int head_dim, void* out, float* lse,
                         hipStream_t stream);

@@ -87,6 +87,19 @@ _SIGS["sink_attn_prefill_split"] = (ctypes.c_int, [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,              # hkv d sc causal
     ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,           # ns ws wsb out
     ctypes.c_void_p, _ROPE_P, ctypes.c_void_p])
+_SIGS["sink_attn_decode_stream_plan"] = (ctypes.c_int32, [
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)])
+_SIGS["sink_attn_decode_stream_partial"] = (ctypes.c_int, [
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+    ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+    _ROPE_P, ctypes.c_void_p])
+_SIGS["sink_attn_decode_stream_merge"] = (ctypes.c_int, [
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+    ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
 _SIGS["sink_attn_prefill_num_splits"] = (ctypes.c_int32, [ctypes.c_int32] * 6)
 _SIGS["sink_attn_prefill_workspace_bytes"] = (ctypes.c_size_t, [
     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32])
@@ -329,6 +342,69 @@ def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optiona
                                       _ptr(part_lse), _rope_arg(rope), _stream(q.device))
     _check(rc)
     return part_o, part_lse
+
+
+def decode_stream_plan(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                       head_dim: int, total_kv: int, max_kv_len: int):
+    """(R, ranges_per_head, slots) of the stream plan decode() uses for these sizes, or
+    None when it uses the chunk plan."""
+    r, n, s = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    ok = load().sink_attn_decode_stream_plan(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                             int(total_kv), int(max_kv_len), ctypes.byref(r),
+                                             ctypes.byref(n), ctypes.byref(s))
+    return (r.value, n.value, s.value) if ok else None
+
+
+def _stream_views(workspace, rows: int, slots: int, d: int):
+    ob = (rows * slots * d * 4 + 255) // 256 * 256
+    po = workspace[: rows * slots * d * 4].view(torch.float32).view(rows, slots, d)
+    pl = workspace[ob: ob + rows * slots * 4].view(torch.float32).view(rows, slots)
+    return po, pl
+
+
+def decode_stream_partial(q, k, v, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,
+                          causal: bool = True, workspace=None, rope: Optional[RopeParams] = None):
+    """First step of the stream plan alone.  Returns (part_o [rows, S, D] fp32, part_lse
+    [rows, S] fp32, workspace): views into the workspace; slot j of a row holds the keys of
+    its sequence in range floor(kv_indptr[b]/R) + j (no sink); slots past the sequence's
+    last range are not written."""
+    lib = load()
+    b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
+    plan = decode_stream_plan(b, ql, hq, hkv, d, tk, max_kv_len)
+    _need(plan is not None, "the stream plan does not apply to these sizes")
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if workspace is None:
+        workspace = decode_workspace(b, ql, hq, hkv, d, max_kv_len, 0, q.device)
+    _dev_tensor(workspace, torch.uint8, "workspace")
+    rc = lib.sink_attn_decode_stream_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), b, ql,
+                                             tk, int(max_kv_len), hq, hkv, d, scale,
+                                             int(bool(causal)), _ptr(workspace),
+                                             workspace.numel(), _rope_arg(rope),
+                                             _stream(q.device))
+    _check(rc)
+    po, pl = _stream_views(workspace, b * ql * hq, plan[2], d)
+    return po, pl, workspace
+
+
+def decode_stream_merge(sinks, kv_indptr, q_shape, total_kv: int, num_kv_heads: int,
+                        max_kv_len: int, workspace, out=None, lse=None):
+    """Second step of the stream plan alone: (out [B, q_len, Hq, D] bf16, lse [B, q_len, Hq])
+    from the partials in `workspace` and the sinks."""
+    lib = load()
+    b, ql, hq, d = q_shape
+    _dev_tensor(kv_indptr, torch.int32, "kv_indptr", 1)
+    _dev_tensor(workspace, torch.uint8, "workspace")
+    sinks = _sinks_arg(sinks, hq, workspace.device)
+    if out is None:
+        out = torch.empty((b, ql, hq, d), dtype=torch.bfloat16, device=workspace.device)
+    if lse is None:
+        lse = torch.empty((b, ql, hq), dtype=torch.float32, device=workspace.device)
+    rc = lib.sink_attn_decode_stream_merge(_ptr(sinks), _ptr(kv_indptr), b, ql, int(total_kv),
+                                           int(max_kv_len), hq, num_kv_heads, d, _ptr(workspace),
+                                           workspace.numel(), _ptr(out), _ptr(lse),
+                                           _stream(workspace.device))
+    _check(rc)
+    return out, lse
 
 
 def merge(part_o, part_lse, out=None, lse=None, return_lse: bool = True):

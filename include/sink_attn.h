@@ -151,6 +151,11 @@ size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, i
  *             sink_attn_decode_chunks_per_slot(...) is the number of chunks one
  *             workgroup takes together; k in 1..64 = exactly k chunks per sequence.  A
  *             chunk holds ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
+ *             With num_splits = 0, q_len * num_q_heads/num_kv_heads <= 16, total_kv <
+ *             2^31 and more than one partial slot (see sink_attn_decode_num_slots), the
+ *             stream plan is used instead: each KV head's token axis (all sequences back
+ *             to back) is cut into equal ranges of R tokens, one wavefront each, whose
+ *             partials are merged with the sinks (sink_attn_decode_stream_plan).
  *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,
  *             256-byte aligned; contents need no initialisation.  Calls that share one
  *             workspace must be stream-ordered.
@@ -168,7 +173,8 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
                      const sink_attn_rope* rope, void* stream);
 
 /* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
- * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot). */
+ * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot): S slots of
+ * the chunk plan, or 17 where the stream plan may be used. */
 size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_kv_len, int32_t num_splits);
@@ -201,6 +207,45 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
                              float sm_scale, int32_t causal, int32_t num_splits,
                              float* part_o, float* part_lse, const sink_attn_rope* rope,
                              void* stream);
+
+/*
+ * Stream plan of sink_attn_decode (contiguous K/V).  "Sink attention": the key axis is
+ * split into blocks merged by their log-sum-exp and the sink is counted once.  Here the
+ * blocks are ranges of R tokens of one KV head's token axis, all sequences back to back:
+ * range i of head g covers tokens [i*R, (i+1)*R) and one wavefront streams it, closing a
+ * partial wherever a sequence ends inside it.  Partial j of row r (sequence b) covers the
+ * keys of b inside range floor(kv_indptr[b]/R) + j and carries no sink; the merge adds
+ * the sink of head h once, as a log-sum-exp term of value zero.
+ *
+ * sink_attn_decode_stream_plan: 1 if the stream plan applies to these sizes (then R, the
+ *   ranges per head and the slots S per row are written where the pointers are not
+ *   NULL), else 0.  R is a multiple of 32, at least ceil(max_kv_len/16), so S <= 17.
+ * sink_attn_decode_stream_partial: the first step on its own, into `workspace` (size and
+ *   alignment as for sink_attn_decode): part_o fp32 [rows, S, head_dim] at offset 0,
+ *   part_lse fp32 [rows, S] at the next 256-byte boundary, rows = batch*q_len*num_q_heads.
+ *   Slots past a row's last range are not written.  Returns SINK_ATTN_ERR_UNSUPPORTED
+ *   where the plan does not apply.
+ * sink_attn_decode_stream_merge: the second step on its own: out / lse from the partials
+ *   in `workspace` and the sinks (NULL = no sink).  A sequence with no keys gets out = 0
+ *   and lse = sink (or -inf).
+ * Both are exported so each step can be checked and timed; sink_attn_decode runs them
+ * back to back.
+ */
+int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
+                                     int32_t max_kv_len, int32_t* range_tokens,
+                                     int32_t* ranges_per_head, int32_t* slots);
+int sink_attn_decode_stream_partial(const void* q, const void* k, const void* v,
+                                    const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                                    int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                    int32_t causal, void* workspace, size_t workspace_bytes,
+                                    const sink_attn_rope* rope, void* stream);
+int sink_attn_decode_stream_merge(const float* sinks, const int32_t* kv_indptr, int32_t batch,
+                                  int32_t q_len, int64_t total_kv, int32_t max_kv_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  const void* workspace, size_t workspace_bytes, void* out,
+                                  float* lse, void* stream);
 
 /*
  * Log-sum-exp merge of chunk partials ("Sink attention": blocks along the key axis are

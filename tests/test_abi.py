@@ -145,7 +145,15 @@ def test_workspace_bytes(lib):
     assert wb(256, 4, 64, 4, 128, 32768, 32) == expect
     rows, s, d = 64 * 64, 4, 64                      # 16 planned chunks in 4 slots
     o = (rows * s * d * 4 + 255) // 256 * 256
+    assert wb(64, 1, 64, 8, 64, 8192, 16) == (o + rows * s * 4 + 255) // 256 * 256
+    # planner mode with <= 16 rows per KV head may take the stream plan: 17 slots
+    s = 17
+    o = (rows * s * d * 4 + 255) // 256 * 256
     assert wb(64, 1, 64, 8, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
+    # 32 rows per KV head (chunk plan only, one chunk per slot): 16 slots
+    rows, s = 64 * 64, 16
+    o = (rows * s * d * 4 + 255) // 256 * 256
+    assert wb(64, 1, 64, 2, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
     assert wb(0, 1, 8, 8, 64, 10, 0) == 0 and wb(1, 5, 8, 8, 64, 10, 0) == 0
     assert wb(1, 1, 8, 8, 96, 10, 0) == 0 and wb(1, 1, 8, 3, 64, 10, 0) == 0
 

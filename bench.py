@@ -101,39 +101,61 @@ def _traffic_for(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def _c_call(fn, args):
+    """One pre-marshalled C-ABI call (no Python argument handling between the events)."""
+    rc = fn(*args)
+    if rc != 0:
+        raise RuntimeError(f"{fn.__name__} failed with status {rc}")
+
+
 def bench_decode(sa, w, steps, warmup, flush):
+    """Mean event times of the whole decode call and of its two kernels alone (the same
+    launches decode makes).  The C entry points are called with arguments marshalled
+    once, so no Python work separates an event from its kernel launch."""
+    from gqa_attention_sink_amd import sink_attn as sam
+    lib = sam.load()
+    P = sam._ptr
+    st = sam._stream(w.q.device)
     ws = sa.decode_workspace(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
     out = torch.empty_like(w.q)
     lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
     s = sa.decode_num_slots(w.q_len, w.hq, w.hkv, w.d, w.max_kv, w.num_splits)
     rows = w.batch * w.q_len * w.hq
-    po = torch.empty((rows, s, w.d), dtype=torch.float32, device="cuda")
-    pl = torch.empty((rows, s), dtype=torch.float32, device="cuda")
+    tk = w.k.shape[1]
+    scale, causal, ns, mk = float(w.scale), int(bool(w.causal)), int(w.num_splits), int(w.max_kv)
+    stream = (sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, w.max_kv)
+              if w.num_splits == 0 else None)
+    full = (lib.sink_attn_decode, (P(w.q), P(w.k), P(w.v), P(w.sinks), P(w.cu_seqlens_kv),
+                                   w.batch, w.q_len, tk, mk, w.hq, w.hkv, w.d, scale, causal, ns,
+                                   P(ws), ws.numel(), P(out), P(lse), None, st))
+    if stream is not None:  # the stream plan's two kernels, as decode runs them
+        part = (lib.sink_attn_decode_stream_partial,
+                (P(w.q), P(w.k), P(w.v), P(w.cu_seqlens_kv), w.batch, w.q_len, tk, mk, w.hq,
+                 w.hkv, w.d, scale, causal, P(ws), ws.numel(), None, st))
+        merge = (lib.sink_attn_decode_stream_merge,
+                 (P(w.sinks), P(w.cu_seqlens_kv), w.batch, w.q_len, tk, mk, w.hq, w.hkv, w.d,
+                  P(ws), ws.numel(), P(out), P(lse), st))
+        po = pl = None
+    else:
+        po = torch.empty((rows, s, w.d), dtype=torch.float32, device="cuda")
+        pl = torch.empty((rows, s), dtype=torch.float32, device="cuda")
+        part = (lib.sink_attn_decode_partial,
+                (P(w.q), P(w.k), P(w.v), P(w.sinks), P(w.cu_seqlens_kv), w.batch, w.q_len, tk,
+                 mk, w.hq, w.hkv, w.d, scale, causal, ns, P(po), P(pl), None, st))
+        merge = (lib.sink_attn_merge, (P(po), P(pl), rows, s, w.d, P(out), P(lse), st))
 
     def step_full(t=None, i=0):
         flush.sum()
         if t: t.mark(i, 0)
-        sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal,
-                  w.num_splits, workspace=ws, out=out, lse=lse)
+        _c_call(*full)
         if t: t.mark(i, 1)
-
-    stream = (sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, w.k.shape[1], w.max_kv)
-              if w.num_splits == 0 else None)
 
     def step_split(t, i):
         flush.sum()
         t.mark(i, 0)
-        if stream is not None:  # the stream plan's two kernels, as decode runs them
-            sa.decode_stream_partial(w.q, w.k, w.v, w.cu_seqlens_kv, w.max_kv, w.scale,
-                                     w.causal, workspace=ws)
-            t.mark(i, 1)
-            sa.decode_stream_merge(w.sinks, w.cu_seqlens_kv, tuple(w.q.shape), w.k.shape[1],
-                                   w.hkv, w.max_kv, ws, out=out, lse=lse)
-        else:
-            sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
-                              w.causal, w.num_splits, part_o=po, part_lse=pl)
-            t.mark(i, 1)
-            sa.merge(po, pl, out=out.view(rows, w.d), lse=lse.view(rows))
+        _c_call(*part)
+        t.mark(i, 1)
+        _c_call(*merge)
         t.mark(i, 2)
 
     for _ in range(warmup):
@@ -146,7 +168,7 @@ def bench_decode(sa, w, steps, warmup, flush):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     full_ms = t.ms(0, 1)
-    # the split kernel on its own (same launches as inside decode)
+    # the two kernels on their own (same launches as inside decode)
     t2 = Timer(steps)
     for i in range(steps):
         step_split(t2, i)
@@ -170,12 +192,26 @@ def bench_prefill(sa, w, steps, warmup, flush, num_splits=1):
         ws = torch.empty(max(256, sa.prefill_workspace_bytes(w.q.shape[0], w.hq, w.d, ns)),
                          dtype=torch.uint8, device="cuda")
 
+    # pre-marshalled C call (no Python argument handling between the events)
+    from gqa_attention_sink_amd import sink_attn as sam
+    lib = sam.load()
+    P = sam._ptr
+    st = sam._stream(w.q.device)
+    tq, tk = w.q.shape[0], w.k.shape[1]
+    common = (P(w.q), P(w.k), P(w.v), P(w.sinks), P(w.cu_seqlens_q), P(w.cu_seqlens_kv),
+              w.batch, int(w.max_q))
+    tail = (tq, tk, w.hq, w.hkv, w.d, float(w.scale), int(bool(w.causal)))
+    if num_splits == 1:
+        call = (lib.sink_attn_prefill, common + tail + (P(out), P(lse), None, st))
+    else:
+        call = (lib.sink_attn_prefill_split,
+                common + (int(w.max_kv),) + tail + (int(num_splits), P(ws), ws.numel(), P(out),
+                                                    P(lse), None, st))
+
     def step(t=None, i=0):
         flush.sum()
         if t: t.mark(i, 0)
-        sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv, w.max_q, w.scale,
-                   w.causal, out=out, lse=lse, num_splits=num_splits, max_seqlen_kv=w.max_kv,
-                   workspace=ws)
+        _c_call(*call)
         if t: t.mark(i, 1)
 
     for _ in range(warmup):
@@ -427,7 +463,18 @@ def main():
         others["spec_decode"] = {"GB/s": round(g5, 2), "frac_of_hbm_peak": round(g5 / HBM_PEAK_GBS, 4),
                                  "ms": round(r5["full_ms"], 4), "split_kernel_GB/s": round(s5, 2),
                                  "split_ms": round(r5["split_ms"], 4),
-                                 "merge_ms": round(r5["merge_ms"], 4), "bytes": b5}
+                                 "merge_ms": round(r5["merge_ms"], 4), "bytes": b5,
+                                 "plan": "32 chunks per sequence (as the workload names)"}
+        # the same batch under the planner (num_splits = 0): the stream plan
+        d5.num_splits = 0
+        r6 = bench_decode(sa, d5, max(5, args.steps // 2), 2, flush)
+        g6 = b5 / (r6["full_ms"] * 1e-3) / 1e9
+        s6 = decode_bytes(d5, True) / (r6["split_ms"] * 1e-3) / 1e9
+        others["spec_decode_planner"] = {
+            "GB/s": round(g6, 2), "frac_of_hbm_peak": round(g6 / HBM_PEAK_GBS, 4),
+            "ms": round(r6["full_ms"], 4), "split_kernel_GB/s": round(s6, 2),
+            "split_ms": round(r6["split_ms"], 4), "merge_ms": round(r6["merge_ms"], 4),
+            "bytes": b5, "plan": r6["plan"], "stream_plan": r6["stream_plan"]}
         del d5
         torch.cuda.empty_cache()
         _say("workload paged decode / kv append")

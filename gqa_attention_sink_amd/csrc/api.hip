@@ -45,21 +45,27 @@ inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
   return sa::decode_chunk_waves(q_len * (hq / hkv), d);
 }
 
-// Stream decode plan (contiguous K/V, at most 16 query rows per KV head, planner mode,
-// more than one partial per row): about 4 wavefronts per CU, each taking R tokens of one
-// KV head's token axis; R is at least max_kv/16 (so a sequence overlaps at most 17
-// ranges, the slots a row needs) and a multiple of 32.
+// Stream decode plan (contiguous K/V, at most 64 query rows per KV head, planner mode,
+// more than one partial per row).  Up to 16 rows: about 4 wavefronts per CU, each taking
+// R tokens of one KV head's token axis; up to 64 rows: about 2 workgroups per CU of 2 or 4
+// wavefronts (16 rows each) sharing each range.  R is at least max_kv/16 (so a sequence
+// overlaps at most 17 ranges, the slots a row needs) and a multiple of 32.
 using sa::kStreamMaxSlots;
 constexpr int kStreamWavesTotal = 4 * 256;
+constexpr int kStreamGroupsTotal = 2 * 256;
 inline bool stream_eligible(int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
                             int32_t max_kv_len, int32_t num_splits) {
-  return num_splits == 0 && q_len * (hq / hkv) <= 16 &&
+  return num_splits == 0 && q_len * (hq / hkv) <= 64 &&
          planned_slots(max_kv_len, num_splits, chunk_waves(q_len, hq, hkv, d)) > 1;
 }
 inline int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
-sa::StreamPlan stream_plan(int32_t batch, int32_t hkv, int64_t total_kv, int32_t max_kv_len) {
+sa::StreamPlan stream_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv,
+                           int64_t total_kv, int32_t max_kv_len) {
   sa::StreamPlan p{};
-  p.nph = kStreamWavesTotal / hkv > 0 ? kStreamWavesTotal / hkv : 1;
+  const int rows = q_len * (hq / hkv);
+  p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int total = p.waves == 1 ? kStreamWavesTotal : kStreamGroupsTotal;
+  p.nph = total / hkv > 0 ? total / hkv : 1;
   int64_t r = round32((total_kv + p.nph - 1) / p.nph);
   const int64_t r_floor = round32((max_kv_len + kStreamMaxSlots - 2) / (kStreamMaxSlots - 1));
   if (r < r_floor) r = r_floor;
@@ -190,7 +196,7 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
                                                          head_dim, max_kv_len, num_splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
       return SINK_ATTN_ERR_WORKSPACE;
-    const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, a.total_kv, max_kv_len);
+    const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, a.total_kv, max_kv_len);
     const int64_t rows = (int64_t)batch * q_len * num_q_heads;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
@@ -449,7 +455,7 @@ int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q
       total_kv > INT32_MAX || max_kv_len < 0 ||
       !stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0))
     return 0;
-  const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, total_kv, max_kv_len);
+  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len);
   if (range_tokens) *range_tokens = sp.R;
   if (ranges_per_head) *ranges_per_head = sp.nph;
   if (slots) *slots = sp.smax;
@@ -478,7 +484,7 @@ static int stream_step(bool partial, const void* q, const void* k, const void* v
                                  num_q_heads, num_kv_heads, head_dim, sm_scale, causal, 0);
   sa::RopeArgs ra;
   if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
-  const sa::StreamPlan sp = stream_plan(batch, num_kv_heads, total_kv, max_kv_len);
+  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len);
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));

@@ -1,4 +1,4 @@
-// Stream decode for q_len * G <= 16 query rows per KV head on contiguous HND K/V.
+// Stream decode for q_len * G <= 64 query rows per KV head on contiguous HND K/V.
 //
 // "GPT-OSS on day 0", "Kernels for GPT-OSS" > "Sink attention": attention is spread over
 // heads and over the key axis; blocks of the key axis merge by their log-sum-exp and the
@@ -297,6 +297,266 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
   wait_vmcnt<0>();  // no copy may land after the wavefront's LDS is released
 }
 
+// The stream plan for 16 < q_len * G <= 64 query rows per KV head: one workgroup of W
+// wavefronts per range (wavefront w owns rows 16w .. 16w+15), all reading every stage of
+// one shared LDS ring (one barrier per stage), so each K/V byte still leaves HBM once per
+// KV head.  Segments, masks, the Q prefetch and the partials are those of
+// decode_stream_kernel; the sequence boundaries are the same for every wavefront.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void decode_stream_wg_kernel(
+    DecodeArgs a, const int32_t* __restrict__ kv_indptr, StreamPlan sp, RopeArgs rope) {
+  constexpr int KS = D / 32;
+  constexpr int DPL = D / 16;
+  constexpr int ROW = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int STEP = 32;
+  constexpr int NST = 3;                     // shared ring stages
+  constexpr int SB = STEP * ROW;
+  constexpr int NDMA = SB / (64 * W * 16);   // copies per lane per tensor per stage
+  static_assert(NDMA * 64 * W * 16 == SB, "stage must split evenly over the workgroup");
+  constexpr int QB = 16 * ROW;
+  constexpr int NQD = QB / (64 * 16);
+  struct Smem {
+    unsigned char ring[NST][2][SB];
+    unsigned char q[W][2][QB];
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int l16 = lane & 15;
+  const int cg = lane >> 4;
+  const int g = (int)blockIdx.x / sp.nph;
+  const int piece = (int)blockIdx.x - g * sp.nph;
+  if (g >= sp.num_kv_heads) return;
+  const int t0 = (int)min<int64_t>((int64_t)piece * sp.R, a.total_kv);
+  const int t1 = (int)min<int64_t>((int64_t)t0 + sp.R, a.total_kv);
+  if (t0 >= t1) return;  // workgroup-uniform: no wavefront reaches a barrier
+
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int M = a.q_len * G;
+  const int B = sp.batch;
+  const int S = sp.smax;
+  auto sbeg = [&](int bb) { return (int)min<int64_t>(max(kv_indptr[bb], 0), a.total_kv); };
+  auto send = [&](int bb) {
+    return (int)min<int64_t>(max(kv_indptr[bb + 1], sbeg(bb)), a.total_kv);
+  };
+  const int R = w * 16 + l16;  // the lane's query row
+  const int row_t = R / G;
+  const int row_h = g * G + (R - row_t * G);
+  const bool row_ok = R < M;
+
+  const int c0 = max(t0, sbeg(0));
+  const int c1 = max(c0, min(t1, send(B - 1)));
+  const size_t head_base = ((size_t)g * a.total_kv + c0) * D;
+  const uint32_t range_bytes = (uint32_t)(c1 - c0) * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, range_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, range_bytes);
+  const int lead = c0 - t0;
+  auto issue = [&](int st) {
+    unsigned char* kbuf = sm.ring[st % NST][0];
+    unsigned char* vbuf = sm.ring[st % NST][1];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int blk = i * W + w;  // 1 KiB block of the stage this wavefront fills
+      const int p = blk * 64 + lane;
+      const int row = p / CPR;
+      const int cc = p - row * CPR;
+      const int tok = st * STEP + row - lead;
+      const uint32_t rbase = tok >= 0 ? (uint32_t)tok * ROW : kNoRead;
+      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+    }
+  };
+  // this wavefront's 16 query rows of sequence bb (bb < 0: zeros)
+  auto issue_q = [&](int bb, int buf) {
+    const uint32_t qbytes = (uint32_t)(a.q_len * Hq * ROW);
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc((const __bf16*)a.q + (size_t)max(bb, 0) * a.q_len * Hq * D, bb >= 0 ? qbytes : 0u);
+#pragma unroll
+    for (int i = 0; i < NQD; ++i) {
+      const int p = i * 64 + lane;
+      const int r = w * 16 + p / CPR;
+      const int rt = r / G;
+      const int rh = g * G + (r - rt * G);
+      const uint32_t off =
+          (r < M) ? (uint32_t)((rt * Hq + rh) * ROW + (p - (p / CPR) * CPR) * 16) : kNoRead;
+      dma16(qr, off, &sm.q[w][buf][i * 1024]);
+    }
+  };
+  auto next_seq = [&](int bb) {
+    bb = __builtin_amdgcn_readfirstlane(bb);
+    while (bb < B && send(bb) <= sbeg(bb)) ++bb;
+    return (int)__builtin_amdgcn_readfirstlane(bb);
+  };
+
+  int lo = 0, hi = B;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (send(mid) <= t0) lo = mid + 1;
+    else hi = mid;
+  }
+  int b = next_seq(lo);
+  bool have = b < B && sbeg(b) < t1;
+  int bn = have ? next_seq(b + 1) : B;
+  bool have_n = bn < B && sbeg(bn) < t1;
+  int kseg = 0;
+  issue_q(have ? b : -1, 0);
+  issue_q(have_n ? bn : -1, 1);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue(st);
+  wait_vmcnt<(NST - 1) * 2 * NDMA>();  // this wavefront's Q tiles (issued first) have landed
+  int q_st = -NST;
+
+  bf16x8 qop[KS];
+  float m = kNegInf, dsum = 0.f;
+  f32x4 o[DPL];
+  int sb = 0, se = 0, lim = 0, causal_first = 0;
+  auto start_segment = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = *(const bf16x8*)&sm.q[w][kseg & 1][l16 * ROW + (ks * 32 + cg * 8) * 2];
+    const int s0 = sbeg(b), e0 = send(b);
+    if (rope.enabled) {
+      const int64_t pos = (int64_t)(e0 - s0) - a.q_len + row_t;
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
+    }
+    sb = max(t0, s0);
+    se = min(t1, e0);
+    lim = min(se - 1, a.causal ? e0 - a.q_len + row_t : 0x7fffffff);
+    causal_first = a.causal ? e0 - a.q_len + 1 : 0x7fffffff;
+    m = kNegInf;
+    dsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto flush_segment = [&]() {
+    float dr = wave_xor_sum(dsum, 16);
+    dr = wave_xor_sum(dr, 32);
+    const int slot = piece - sbeg(b) / sp.R;
+    if (!row_ok || slot < 0 || slot >= S) return;
+    const float inv = dr > 0.f ? 1.0f / dr : 0.f;
+    const int64_t qrow = ((int64_t)b * a.q_len + row_t) * Hq + row_h;
+    float* dst = a.part_o + (qrow * S + slot) * D + 4 * cg * DPL;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < DPL; t += 4)
+        *(f32x4*)(dst + j * DPL + t) = f32x4{o[t][j] * inv, o[t + 1][j] * inv, o[t + 2][j] * inv,
+                                             o[t + 3][j] * inv};
+    if (cg == 0) a.part_lse[qrow * S + slot] = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
+  };
+  if (have) start_segment();
+
+  const float sl2 = a.scale_log2;
+  const int nsteps = (t1 - t0 + STEP - 1) / STEP;
+  for (int st = 0; st < nsteps; ++st) {
+    // stage st has landed (this wavefront's copies) once only the NST-2 stages issued
+    // after it are pending; after the barrier every wavefront's copies have, and every
+    // wavefront has finished stage st-1, whose slot is refilled
+    wait_vmcnt<(NST - 2) * 2 * NDMA>();
+    stage_barrier();
+    issue(st + NST - 1);
+    const unsigned char* kbuf = sm.ring[st % NST][0];
+    const unsigned char* vbuf = sm.ring[st % NST][1];
+    const int kbase = t0 + st * STEP;
+
+    while (have && sb < kbase + STEP) {
+      f32x4 s2[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int row = kt * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kv = *(const u32x4*)(kbuf + row * ROW + (((ks * 4 + cg) ^ dswz<D>(row)) * 16));
+          acc = mfma16(as_bf16x8(kv), qop[ks], acc);
+        }
+        s2[kt] = acc;
+      }
+      if (kbase < sb || kbase + STEP > se || kbase + STEP > causal_first) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = kbase + kt * 16 + 4 * cg + j;
+            s2[kt][j] = (key >= sb && key <= lim) ? s2[kt][j] : kNegInf;
+          }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                       fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+      mx = max_over_16_32(mx);
+      const float mxs = mx * sl2;
+      if (__any(mxs > m + 8.0f)) {
+        const float mnew = fmaxf(m, mxs);
+        const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+        dsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) o[t] *= alpha;
+        m = mnew;
+      }
+      const float msub = (m == kNegInf) ? 0.0f : m;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = fast_exp2(__builtin_fmaf(s2[0][j], sl2, -msub));
+        p[4 + j] = fast_exp2(__builtin_fmaf(s2[1][j], sl2, -msub));
+      }
+      dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      u32x4 pk;
+      pk.x = pack_bf16x2(p[0], p[1]);
+      pk.y = pack_bf16x2(p[2], p[3]);
+      pk.z = pack_bf16x2(p[4], p[5]);
+      pk.w = pack_bf16x2(p[6], p[7]);
+      const bf16x8 pop = as_bf16x8(pk);
+      uint32_t vw[8][DPL / 2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned char* src = vbuf + slot_key(cg, i) * ROW + l16 * DPL * 2;
+        if constexpr (DPL == 8) {
+          const u32x4 t4 = *(const u32x4*)src;
+          vw[i][0] = t4.x; vw[i][1] = t4.y; vw[i][2] = t4.z; vw[i][3] = t4.w;
+        } else {
+          const u32x2 t2 = *(const u32x2*)src;
+          vw[i][0] = t2.x; vw[i][1] = t2.y;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) {
+        u32x4 va;
+        const int wd = t >> 1;
+        if ((t & 1) == 0) {
+          va.x = lo_lo(vw[0][wd], vw[1][wd]);
+          va.y = lo_lo(vw[2][wd], vw[3][wd]);
+          va.z = lo_lo(vw[4][wd], vw[5][wd]);
+          va.w = lo_lo(vw[6][wd], vw[7][wd]);
+        } else {
+          va.x = hi_hi(vw[0][wd], vw[1][wd]);
+          va.y = hi_hi(vw[2][wd], vw[3][wd]);
+          va.z = hi_hi(vw[4][wd], vw[5][wd]);
+          va.w = hi_hi(vw[6][wd], vw[7][wd]);
+        }
+        o[t] = mfma16(as_bf16x8(va), pop, o[t]);
+      }
+      if (se > kbase + STEP) break;
+      flush_segment();
+      b = bn;
+      have = have_n;
+      if (!have) break;
+      ++kseg;
+      if (st < q_st + NST - 1) wait_vmcnt<0>();
+      start_segment();
+      bn = next_seq(b + 1);
+      have_n = bn < B && sbeg(bn) < t1;
+      issue_q(have_n ? bn : -1, (kseg + 1) & 1);
+      q_st = st;
+    }
+  }
+  wait_vmcnt<0>();
+}
+
 // Merge of the stream partials: row (b, t, h) combines the partials of the ranges that
 // overlap sequence b with the sink of head h, a term of value zero and log-sum-exp
 // sink[h].  D/4 lanes per row, four consecutive head dims each.  All of a row's loads
@@ -365,6 +625,21 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
 
 hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
                                 const RopeArgs& rope, hipStream_t stream) {
+  if (sp.waves > 1) {  // one workgroup of sp.waves wavefronts per range
+    const dim3 grid((unsigned)(sp.num_kv_heads * sp.nph));
+    if (head_dim == 64) {
+      if (sp.waves == 2)
+        hipLaunchKernelGGL((decode_stream_wg_kernel<64, 2>), grid, dim3(128), 0, stream, a, a.kv_indptr, sp, rope);
+      else
+        hipLaunchKernelGGL((decode_stream_wg_kernel<64, 4>), grid, dim3(256), 0, stream, a, a.kv_indptr, sp, rope);
+    } else {
+      if (sp.waves == 2)
+        hipLaunchKernelGGL((decode_stream_wg_kernel<128, 2>), grid, dim3(128), 0, stream, a, a.kv_indptr, sp, rope);
+      else
+        hipLaunchKernelGGL((decode_stream_wg_kernel<128, 4>), grid, dim3(256), 0, stream, a, a.kv_indptr, sp, rope);
+    }
+    return hipGetLastError();
+  }
   const int waves = sp.num_kv_heads * sp.nph;
   const dim3 grid((unsigned)((waves + kStreamWaves - 1) / kStreamWaves));
   if (head_dim == 64)

@@ -86,8 +86,8 @@ struct AppendArgs {
 };
 
 // Stream decode plan: the token axis of each KV head is cut into ranges of R tokens (a
-// multiple of 32), nph ranges per head, one wavefront each; a row's partials occupy
-// smax slots ([rows, smax, D] outputs then [rows, smax] lse).
+// multiple of 32), nph ranges per head, one wavefront (or one workgroup) each; a row's
+// partials occupy smax slots ([rows, smax, D] outputs then [rows, smax] lse).
 constexpr int kStreamMaxSlots = 17;  // partial slots a row can need under the stream plan
 struct StreamPlan {
   int32_t R;
@@ -95,6 +95,8 @@ struct StreamPlan {
   int32_t smax;
   int32_t batch;
   int32_t num_kv_heads;
+  int32_t waves;  // 1: independent wavefronts, one range each (<= 16 rows); 2 or 4:
+                  // one workgroup of that many wavefronts per range (<= 32 / <= 64 rows)
 };
 
 // Wavefronts per decode workgroup (16 query rows each) for M rows sharing a KV head.
@@ -120,7 +122,7 @@ hipError_t launch_kv_append(const AppendArgs& a, int head_dim, int batch, int ma
 hipError_t launch_rope_apply(void* x, int64_t tokens, int heads, int head_dim,
                              int64_t token_stride, int64_t head_stride,
                              const int32_t* positions, const RopeArgs& rope, hipStream_t stream);
-// Stream decode (contiguous K/V, q_len * G <= 16): partials into a.part_o / a.part_lse,
+// Stream decode (contiguous K/V, q_len * G <= 64): partials into a.part_o / a.part_lse,
 // then their merge with the sinks into a.out / a.lse.
 hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
                                 const RopeArgs& rope, hipStream_t stream);

@@ -150,10 +150,10 @@ def test_workspace_bytes(lib):
     s = 17
     o = (rows * s * d * 4 + 255) // 256 * 256
     assert wb(64, 1, 64, 8, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
-    # 32 rows per KV head (chunk plan only, one chunk per slot): 16 slots
-    rows, s = 64 * 64, 16
+    # 128 rows per KV head (chunk plan only, one chunk per slot): 16 slots
+    rows, s = 64 * 4 * 64, 16
     o = (rows * s * d * 4 + 255) // 256 * 256
-    assert wb(64, 1, 64, 2, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
+    assert wb(64, 4, 64, 2, 64, 8192, 0) == (o + rows * s * 4 + 255) // 256 * 256
     assert wb(0, 1, 8, 8, 64, 10, 0) == 0 and wb(1, 5, 8, 8, 64, 10, 0) == 0
     assert wb(1, 1, 8, 8, 96, 10, 0) == 0 and wb(1, 1, 8, 3, 64, 10, 0) == 0
 

@@ -42,6 +42,8 @@ def lib():
     (300, 2, 16, 4, 128, 3000, 1100),     # many short sequences
     (7, 4, 16, 4, 64, 20000, 5000),
     (3, 1, 8, 1, 64, 2000, 1500),
+    (256, 4, 64, 4, 128, 256 * 32768, 32768),   # speculative decode: 64 rows, 4 waves
+    (9, 2, 32, 2, 64, 30000, 9000),              # 32 rows, 2 waves
 ])
 def test_stream_plan_properties(lib, b, ql, hq, hkv, d, total, maxkv):
     plan = sa_mod.decode_stream_plan(b, ql, hq, hkv, d, total, maxkv)
@@ -62,7 +64,7 @@ def test_stream_plan_properties(lib, b, ql, hq, hkv, d, total, maxkv):
 
 
 @pytest.mark.parametrize("b,ql,hq,hkv,d,total,maxkv", [
-    (4, 1, 64, 2, 64, 8000, 2000),    # 32 rows per KV head: chunk plan
+    (4, 4, 64, 2, 64, 8000, 2000),    # 128 rows per KV head: chunk plan
     (4, 1, 64, 8, 64, 4000, 1024),    # one slot: the chunk kernel writes the result
 ])
 def test_stream_plan_not_used(lib, b, ql, hq, hkv, d, total, maxkv):
@@ -78,8 +80,8 @@ def test_stream_partial_rejects(lib):
     need = sa_mod.decode_workspace_bytes(4, 1, 64, 8, 64, 2000, 0)
     assert lib.sink_attn_decode_stream_partial(*args, sa_mod.ctypes.c_void_p(0x1010), need,
                                                None, None) == 3
-    # 32 rows per KV head: the stream plan does not apply
-    args2 = [fake, fake, fake, fake, 4, 1, 8000, 2000, 64, 2, 64, 0.1, 1]
+    # 128 rows per KV head: the stream plan does not apply (rejected before any launch)
+    args2 = [fake, fake, fake, fake, 4, 2, 8000, 2000, 64, 1, 64, 0.1, 1]
     assert lib.sink_attn_decode_stream_partial(*args2, fake, 1 << 30, None, None) == 2
     # merge: missing output
     assert lib.sink_attn_decode_stream_merge(None, fake, 4, 1, 8000, 2000, 64, 8, 64, fake,
@@ -134,6 +136,10 @@ STREAM_CASES = [
     ([50] * 40 + [1300], 2, 16, 2, 128, ("normal", 0, 2), True),
     ([4096, 2500, 1025], 4, 16, 4, 128, None, True),
     ([1500, 800, 3000], 1, 8, 1, 64, ("normal", 0, 2), False),
+    # more than 16 rows per KV head: one workgroup of 2 or 4 wavefronts per range
+    ([3000, 40, 1, 1200, 0, 5000], 4, 64, 4, 128, ("normal", 0, 2), True),      # 64 rows
+    ([700, 33, 2100, 64, 5], 2, 32, 2, 64, ("alt_neginf", 2, 1), True),         # 32 rows
+    ([1800, 90, 2600], 3, 32, 2, 128, ("normal", 0, 2), True),                  # 48 rows
 ]
 
 

@@ -151,11 +151,13 @@ size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, i
  *             sink_attn_decode_chunks_per_slot(...) is the number of chunks one
  *             workgroup takes together; k in 1..64 = exactly k chunks per sequence.  A
  *             chunk holds ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
- *             With num_splits = 0, q_len * num_q_heads/num_kv_heads <= 16, total_kv <
+ *             With num_splits = 0, q_len * num_q_heads/num_kv_heads <= 64, total_kv <
  *             2^31 and more than one partial slot (see sink_attn_decode_num_slots), the
  *             stream plan is used instead: each KV head's token axis (all sequences back
- *             to back) is cut into equal ranges of R tokens, one wavefront each, whose
- *             partials are merged with the sinks (sink_attn_decode_stream_plan).
+ *             to back) is cut into equal ranges of R tokens, each streamed by one
+ *             wavefront (<= 16 rows) or by one workgroup of 2 or 4 wavefronts that
+ *             share the staged keys (<= 32 / <= 64 rows), whose partials are merged
+ *             with the sinks (sink_attn_decode_stream_plan).
  *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,
  *             256-byte aligned; contents need no initialisation.  Calls that share one
  *             workspace must be stream-ordered.
@@ -212,7 +214,8 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
  * Stream plan of sink_attn_decode (contiguous K/V).  "Sink attention": the key axis is
  * split into blocks merged by their log-sum-exp and the sink is counted once.  Here the
  * blocks are ranges of R tokens of one KV head's token axis, all sequences back to back:
- * range i of head g covers tokens [i*R, (i+1)*R) and one wavefront streams it, closing a
+ * range i of head g covers tokens [i*R, (i+1)*R) and one wavefront (or a workgroup of 2
+ * or 4 for more than 16 query rows per KV head, each owning 16 rows) streams it, closing a
  * partial wherever a sequence ends inside it.  Partial j of row r (sequence b) covers the
  * keys of b inside range floor(kv_indptr[b]/R) + j and carries no sink; the merge adds
  * the sink of head h once, as a log-sum-exp term of value zero.

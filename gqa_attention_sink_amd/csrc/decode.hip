@@ -156,8 +156,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
         const int tok0 = t0 + blk * (64 / CPR);  // first row of this copy instruction
         const bool second = tok0 / ps != pa;
         const uint32_t rbase = (uint32_t)(t0 + row - (pa + (second ? 1 : 0)) * ps) * ROW;
-        dma16(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
-        dma16(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+        dma16_nt(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+        dma16_nt(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
       }
     } else {
 #pragma unroll
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
         const int row = p / CPR;
         const int cc = p - row * CPR;
         const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
-        dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
-        dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+        dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+        dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
       }
     }
   };
@@ -442,8 +442,8 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
         const int tok0 = t0 + i * (64 / CPR);
         const bool second = tok0 / ps != pa;
         const uint32_t rbase = (uint32_t)(t0 + row - (pa + (second ? 1 : 0)) * ps) * ROW;
-        dma16(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
-        dma16(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+        dma16_nt(second ? kb2 : ka, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16_nt(second ? vb2 : va, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
       }
     } else {
 #pragma unroll
@@ -452,8 +452,8 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
         const int row = p / CPR;
         const int cc = p - row * CPR;
         const uint32_t rbase = (uint32_t)(st * STEP + row) * ROW;
-        dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
-        dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+        dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
       }
     }
   };

@@ -97,8 +97,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
       const int cc = p - row * CPR;
       const int tok = st * STEP + row - lead;  // token relative to the view
       const uint32_t rbase = tok >= 0 ? (uint32_t)tok * ROW : kNoRead;
-      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
-      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+      dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
     }
   };
   // Q tile of sequence bb (rows past M, or bb < 0, read nothing and land as zeros).
@@ -365,8 +365,8 @@ __global__ __launch_bounds__(64 * W) void decode_stream_wg_kernel(
       const int cc = p - row * CPR;
       const int tok = st * STEP + row - lead;
       const uint32_t rbase = tok >= 0 ? (uint32_t)tok * ROW : kNoRead;
-      dma16(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
-      dma16(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
+      dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + blk * 1024);
+      dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + blk * 1024);
     }
   };
   // this wavefront's 16 query rows of sequence bb (bb < 0: zeros)

@@ -52,6 +52,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
 }
+// The same copy with the non-temporal cache policy (nt), for data read once per launch:
+// streamed this way HBM delivers ~6.7-6.8 TB/s to 1024 wavefronts against ~5.9 TB/s with
+// the default policy (measured with plain register loads and with LDS rings alike).
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, kCachePolicyNT);
+}
 
 // The same bounded view as four descriptor words in scalar registers (base address,
 // stride 0, size in bytes, raw-buffer word 3), for the assembly copy below.

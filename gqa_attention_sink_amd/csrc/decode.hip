@@ -665,7 +665,8 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
 // partial outputs are read as whole 16-byte vectors and a wavefront covers 256/D rows.
 // Slots are taken four at a time: the four loads are issued together, and a group
 // whose weights are all zero is skipped.  A slot with lse = -inf has weight 0 and its
-// partial output (possibly never written) is selected away, never multiplied.
+// partial output (possibly never written) is selected away, never multiplied.  The
+// partials are read once, with the non-temporal cache policy.
 constexpr int kMergeThreads = 128;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
@@ -680,18 +681,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const float* pl = part_lse + row * S;
   const f32x4* po = (const f32x4*)(part_o + row * S * D) + q;
   float mx = kNegInf;
-  for (int c = 0; c < S; ++c) mx = fmaxf(mx, pl[c]);
+  for (int c = 0; c < S; ++c) mx = fmaxf(mx, __builtin_nontemporal_load(pl + c));
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != kNegInf) {
     for (int c = 0; c < S; c += 4) {
       float w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = (c + u < S) ? __expf(pl[c + u] - mx) : 0.f;
+      for (int u = 0; u < 4; ++u) w[u] = (c + u < S) ? __expf(__builtin_nontemporal_load(pl + c + u) - mx) : 0.f;
       if ((w[0] + w[1]) + (w[2] + w[3]) == 0.f) continue;
       f32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = po[(size_t)min(c + u, S - 1) * (D / 4)];
+      for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(po + (size_t)min(c + u, S - 1) * (D / 4));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         wsum += w[u];

@@ -560,8 +560,8 @@ __global__ __launch_bounds__(64 * W) void decode_stream_wg_kernel(
 // Merge of the stream partials: row (b, t, h) combines the partials of the ranges that
 // overlap sequence b with the sink of head h, a term of value zero and log-sum-exp
 // sink[h].  D/4 lanes per row, four consecutive head dims each.  All of a row's loads
-// (at most kStreamMaxSlots slots) are issued together, so a row waits for one memory
-// latency, not one per slot.
+// (at most kStreamMaxSlots slots, read once: non-temporal) are issued together, so a row
+// waits for one memory latency, not one per slot.
 template <int D>
 __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamPlan sp,
                                                            int64_t rows) {
@@ -581,10 +581,10 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
   float lc[kStreamMaxSlots];
   f32x4 x[kStreamMaxSlots];
 #pragma unroll
-  for (int c = 0; c < kStreamMaxSlots; ++c) lc[c] = (c < S) ? pl[c] : kNegInf;
+  for (int c = 0; c < kStreamMaxSlots; ++c) lc[c] = (c < S) ? __builtin_nontemporal_load(pl + c) : kNegInf;
 #pragma unroll
   for (int c = 0; c < kStreamMaxSlots; ++c)
-    x[c] = (c < S) ? po[(size_t)c * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+    x[c] = (c < S) ? __builtin_nontemporal_load(po + (size_t)c * (D / 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
   const float sink = (a.sinks != nullptr) ? a.sinks[h] : kNegInf;
   const int s0 = seq_begin(a, b), e0 = seq_end(a, b);
   const int n = (e0 > s0) ? min(S, (e0 - 1) / sp.R - s0 / sp.R + 1) : 0;

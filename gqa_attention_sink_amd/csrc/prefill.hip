@@ -577,8 +577,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
   // S^T of a unit the wavefront does not need is computed and ignored, and the
   // probabilities of a unit it skips are zero, so that unit's V^T.P^T adds nothing.
   // The first step reads the V slot of unit 0 (landed, finite) with zero probabilities.
+  // The wavefront in its matrix phase runs at the higher issue priority, so its MFMAs
+  // are not held back behind the other wavefront's vector work (measured +2.4 %).
   auto matrix_phase = [&](int j) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(3);
     matrix_ops(j, j > 0 ? j - 1 : 0, j, std::true_type{}, std::true_type{});
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // vector phase of relative unit j

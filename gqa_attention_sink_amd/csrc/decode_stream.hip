@@ -8,8 +8,9 @@
 // through its own LDS ring without a break; wherever a sequence begins or ends inside
 // the range it closes the current partial (the online-softmax state of that sequence's
 // keys in the range) and starts the next sequence's with that sequence's queries.  Every
-// wavefront reads the same number of bytes, so the grid finishes together, and each
-// wavefront's reads are one contiguous stream of K and one of V.
+// wavefront reads the same number of bytes (no tail of short chunks; what remains is
+// HBM serving the XCDs at uneven rates), and each wavefront's reads are one contiguous
+// stream of K and one of V, copied with the non-temporal cache policy.
 //
 // Partials carry no sink: the sink of head h enters once, in the merge, as one more
 // log-sum-exp term with value zero (equivalent to counting it in the first block, and it

@@ -604,36 +604,54 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
           sc[kt][i] = (key <= lim) ? sc[kt][i] : kNegInf;
         }
     }
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    // Probabilities against the running max, in groups of 8 (bf16 operands and fp32 group
+    // sums).  The running max is raised when a row's max exceeds it by more than 2^8; if
+    // no group sum exceeds 128, no probability does, so that test would fail and these
+    // probabilities stand: the row max is only computed when some group sum is larger
+    // (or overflowed), or while the running max is still -inf (a -inf sink before the
+    // row's first finite score), where the test always raises it.
+    float gs[2][2];
+    auto probs = [&]() __attribute__((always_inline)) {
+      const float msub = (m == kNegInf) ? 0.0f : m;
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[0][i]), sc[0][i + 1]);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[1][i]), sc[1][i + 1]);
-    const float mxs = half_swap_max(mx) * sl2;
-    if (__any(mxs > m + 8.0f)) {
-      const float mnew = fmaxf(m, mxs);
-      const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
-      dsum *= alpha;
+        for (int kk = 0; kk < 2; ++kk) {
+          float p[8];
 #pragma unroll
-      for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
-      m = mnew;
-    }
-    const float msub = (m == kNegInf) ? 0.0f : m;
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sc[kt][kk * 8 + i], sl2, -msub));
+          u32x4 w4;
+          w4.x = pack_bf16x2(p[0], p[1]);
+          w4.y = pack_bf16x2(p[2], p[3]);
+          w4.z = pack_bf16x2(p[4], p[5]);
+          w4.w = pack_bf16x2(p[6], p[7]);
+          gs[kt][kk] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          pk[kt][kk] = as_bf16x8(w4);
+        }
+    };
+    probs();
+    const float gmax = fmaxf(fmaxf(gs[0][0], gs[0][1]), fmaxf(gs[1][0], gs[1][1]));
+    if (__any(!(gmax <= 128.0f) || m == kNegInf)) {
+      float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[0][i]), sc[0][i + 1]);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float p[8];
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[1][i]), sc[1][i + 1]);
+      const float mxs = half_swap_max(mx) * sl2;
+      if (__any(mxs > m + 8.0f)) {
+        const float mnew = fmaxf(m, mxs);
+        const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+        dsum *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sc[kt][kk * 8 + i], sl2, -msub));
-        u32x4 w4;
-        w4.x = pack_bf16x2(p[0], p[1]);
-        w4.y = pack_bf16x2(p[2], p[3]);
-        w4.z = pack_bf16x2(p[4], p[5]);
-        w4.w = pack_bf16x2(p[6], p[7]);
-        dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pk[kt][kk] = as_bf16x8(w4);
+        for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+        m = mnew;
+        probs();
       }
+    }
+    dsum += gs[0][0];
+    dsum += gs[0][1];
+    dsum += gs[1][0];
+    dsum += gs[1][1];
   };
 
   // Half-phase h: group 0 runs the matrix phase of unit j at h = 2j and its vector phase

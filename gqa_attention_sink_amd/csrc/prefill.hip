@@ -231,39 +231,54 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, RopeArgs
             s[kt][j] = (key <= lim) ? s[kt][j] : kNegInf;
           }
       }
-      // ---- row max; the running max is raised only when it grows by more than 2^8
-      float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-      for (int j = 2; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[0][j]), s[0][j + 1]);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[1][j]), s[1][j + 1]);
-      const float mxs = half_swap_max(mx) * sl2;
-      if (__any(mxs > m + 8.0f)) {
-        const float mnew = fmaxf(m, mxs);
-        const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
-        dsum *= alpha;
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
-        m = mnew;
-      }
-      const float msub = (m == kNegInf) ? 0.0f : m;
-      // ---- probabilities as bf16 B operands; row sums in fp32 before rounding
+      // ---- probabilities as bf16 B operands against the running max, with fp32 sums of
+      // each group of 8.  The running max is raised only when the row max exceeds it by
+      // more than 2^8; if no group sum exceeds 128 no probability does, so the row max is
+      // only computed when some sum is larger (or overflowed), or while the running max
+      // is still -inf (a -inf sink before the row's first finite score).
       bf16x8 pk[2][2];  // [kt][kk]
+      float gs[2][2];
+      auto probs = [&]() __attribute__((always_inline)) {
+        const float msub = (m == kNegInf) ? 0.0f : m;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          float p[8];
+          for (int kk = 0; kk < 2; ++kk) {
+            float p[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[kt][kk * 8 + i], sl2, -msub));
-          u32x4 w4;
-          w4.x = pack_bf16x2(p[0], p[1]);
-          w4.y = pack_bf16x2(p[2], p[3]);
-          w4.z = pack_bf16x2(p[4], p[5]);
-          w4.w = pack_bf16x2(p[6], p[7]);
-          dsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          pk[kt][kk] = as_bf16x8(w4);
+            for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[kt][kk * 8 + i], sl2, -msub));
+            u32x4 w4;
+            w4.x = pack_bf16x2(p[0], p[1]);
+            w4.y = pack_bf16x2(p[2], p[3]);
+            w4.z = pack_bf16x2(p[4], p[5]);
+            w4.w = pack_bf16x2(p[6], p[7]);
+            gs[kt][kk] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            pk[kt][kk] = as_bf16x8(w4);
+          }
+      };
+      probs();
+      const float gmax = fmaxf(fmaxf(gs[0][0], gs[0][1]), fmaxf(gs[1][0], gs[1][1]));
+      if (__any(!(gmax <= 128.0f) || m == kNegInf)) {
+        float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int j = 2; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[0][j]), s[0][j + 1]);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[1][j]), s[1][j + 1]);
+        const float mxs = half_swap_max(mx) * sl2;
+        if (__any(mxs > m + 8.0f)) {
+          const float mnew = fmaxf(m, mxs);
+          const float alpha = (mnew == kNegInf) ? 1.0f : fast_exp2(m - mnew);
+          dsum *= alpha;
+#pragma unroll
+          for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+          m = mnew;
+          probs();
         }
+      }
+      dsum += gs[0][0];
+      dsum += gs[0][1];
+      dsum += gs[1][0];
+      dsum += gs[1][1];
       // ---- O^T += V^T . P^T.  Slot i of 16-key step (kt, kk) for k-group cg is key
       // kt*32 + 16*kk + 8*(i/4) + 4*cg + i%4, read transposed from LDS: for half h of
       // the slots, lane p of each 16-lane group supplies key row

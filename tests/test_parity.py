@@ -113,6 +113,73 @@ def test_prefill_cases(sa, case):
     _compare(out, lse, ro, rl, f"prefill case {case}")
 
 
+def _grow(w, q_gain=4.0, k_gain=5.0):
+    """Scale key j of each sequence by 1 + k_gain*j/len and q by q_gain (then round to
+    bf16 again), so that a row's scores climb along the keys: the running max is raised
+    by more than 2^8 several times after the first 64-key unit, which N(0,1) inputs
+    rarely do.  Kernel and oracle read the same rounded tensors."""
+    cu = w.cu_seqlens_kv.tolist()
+    fac = torch.ones(w.k.shape[1], dtype=torch.float32, device=w.k.device)
+    for b in range(len(cu) - 1):
+        n = cu[b + 1] - cu[b]
+        fac[cu[b]:cu[b + 1]] = 1.0 + k_gain * torch.arange(n, device=w.k.device) / max(n, 1)
+    w.k.copy_((w.k.float() * fac[None, :, None]).to(torch.bfloat16))
+    w.q.copy_((w.q.float() * q_gain).to(torch.bfloat16))
+    # the last query row of the longest sequence, head 0: its max score over all keys
+    # exceeds that over the first 64 keys by more than 8 (log2 units)
+    b = max(range(len(cu) - 1), key=lambda i: cu[i + 1] - cu[i])
+    qrow = w.q.reshape(-1, w.hq, w.d)[w.cu_seqlens_q[b + 1].item() - 1, 0].float()
+    sc = (w.k[0, cu[b]:cu[b + 1]].float() @ qrow) * w.scale * math.log2(math.e)
+    assert sc.max() - sc[:64].max() > 8.0, "inputs do not force a later rescale"
+
+
+GROWTH_PREFILL = [
+    # lens_q, lens_kv, hq, hkv, d, sink, causal
+    ([400, 130], [400, 130], 8, 2, 64, ("normal", 0, 2), True),
+    ([400, 130], [400, 130], 8, 2, 128, ("alt_neginf", 2, 1), True),
+    ([300], [300], 8, 1, 128, ("normal", 0, 2), True),
+    ([90, 150], [500, 260], 8, 2, 64, ("alt_neginf", 2, 1), False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROWTH_PREFILL)))
+def test_prefill_rescale_growth(sa, case):
+    """Scores growing along the keys: the conditional rescale of the running max (and the
+    shortcut that skips the row max while no probability exceeds 128) against the oracle."""
+    lq, lk, hq, hkv, d, sink, causal = GROWTH_PREFILL[case]
+    _say(f"prefill growth case {case}: lq={lq} lk={lk} d={d} sink={sink} causal={causal}")
+    w = wl.make_prefill(lq, lk, hq, hkv, d, sink, 1 / math.sqrt(d), causal, seed=150 + case,
+                        device="cuda")
+    _grow(w)
+    out, lse = _run_prefill(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_prefill(w)
+    _compare(out, lse, ro, rl, f"prefill growth case {case}")
+
+
+GROWTH_DECODE = [
+    # lens_kv, q_len, hq, hkv, d, sink, causal, num_splits
+    ([700, 1500, 90], 1, 64, 8, 64, ("normal", 0, 2), True, 0),
+    ([700, 1500, 90], 4, 64, 4, 128, ("alt_neginf", 2, 1), True, 0),
+    ([900, 333], 1, 8, 2, 64, ("alt_neginf", 2, 1), True, 3),
+    ([900, 333], 4, 64, 4, 128, ("normal", 0, 2), True, 5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROWTH_DECODE)))
+def test_decode_rescale_growth(sa, case):
+    """Decode with scores growing along the keys (rescales inside chunks and ranges)."""
+    lens, ql, hq, hkv, d, sink, causal, ns = GROWTH_DECODE[case]
+    _say(f"decode growth case {case}: lens={lens} q_len={ql} hq={hq} hkv={hkv} d={d} ns={ns}")
+    w = wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, ns,
+                       seed=250 + case, device="cuda")
+    _grow(w)
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_decode(w)
+    _compare(out, lse, ro, rl, f"decode growth case {case}")
+
+
 def test_prefill_varlen_config_reduced(sa):
     """The varlen workload's shape (8 sequences, Hq 64, Hkv 8, D 64) with shorter lengths
     so the oracle checks every output."""

@@ -98,6 +98,9 @@ PREFILL_CASES = [
     ([33, 97], [33, 97], 8, 2, 64, ("normal", 8, 1), True),                 # sink-dominant
     ([300], [300], 64, 4, 128, ("alt_neginf", 2, 1), True),                 # long-prefill shape
     ([257, 511], [257, 511], 64, 8, 64, ("normal", 0, 2), True),            # varlen shape
+    ([5, 30, 3], [0, 40, 0], 8, 2, 64, ("normal", 0, 2), False),            # keyless rows
+    ([5, 30, 3], [0, 40, 0], 8, 2, 128, ("alt_neginf", 2, 1), False),       # keyless, -inf
+    ([64, 0, 70], [64, 0, 70], 8, 2, 128, ("normal", 0, 2), True),          # empty sequence
 ]
 
 

@@ -39,12 +39,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
 
 // Asynchronous 16-byte copy global -> LDS (no registers): lane i of the wavefront
 // writes its 16 bytes at lds_wave_base + 16*i.  lds_wave_base must be wave-uniform.
@@ -121,17 +115,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// fp32 -> bf16 with round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
-}
+// Two fp32 values -> a packed bf16 pair (lo in bits 0-15), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-// acc + lo16(x) + hi16(x) for a packed bf16 pair (sum in fp32).
-__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
 }
 // max / sum over the two lanes l and l^32 (the two halves of the wavefront).
 __device__ __forceinline__ float half_swap_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
@@ -153,9 +139,6 @@ __device__ __forceinline__ float max_over_16_32(float v) {
   return fmaxf(c, e);
 }
 
-__device__ __forceinline__ float wave_xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }

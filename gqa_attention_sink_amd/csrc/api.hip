@@ -190,21 +190,25 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
                const int32_t* page_ids, const sa::RopeArgs& rope, void* workspace,
                size_t workspace_bytes, void* out, float* lse, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  if (page_ids == nullptr && a.total_kv <= INT32_MAX &&
+  // A paged cache streams along its page list laid end to end (single-wavefront plans).
+  const bool paged = page_ids != nullptr;
+  const int64_t axis = paged ? a.num_page_entries * (int64_t)a.page_size : a.total_kv;
+  if (axis <= INT32_MAX && (!paged || q_len * (num_q_heads / num_kv_heads) <= 16) &&
       stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits)) {
     const size_t need = sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads,
                                                          head_dim, max_kv_len, num_splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
       return SINK_ATTN_ERR_WORKSPACE;
-    const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, a.total_kv, max_kv_len);
+    const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, axis, max_kv_len);
+    a.total_kv = axis;
     const int64_t rows = (int64_t)batch * q_len * num_q_heads;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
     a.out = out;
     a.lse = lse;
-    hipError_t e = sa::launch_decode_stream(a, head_dim, sp, rope, st);
+    hipError_t e = sa::launch_decode_stream(a, head_dim, sp, rope, page_ids, st);
     if (e != hipSuccess) return hip_fail(e);
-    e = sa::launch_merge_stream(a, head_dim, sp, rows, st);
+    e = sa::launch_merge_stream(a, head_dim, sp, rows, paged, st);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   }
@@ -490,8 +494,8 @@ static int stream_step(bool partial, const void* q, const void* k, const void* v
   a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
   a.out = out;
   a.lse = lse;
-  hipError_t e = partial ? sa::launch_decode_stream(a, head_dim, sp, ra, (hipStream_t)stream)
-                         : sa::launch_merge_stream(a, head_dim, sp, rows, (hipStream_t)stream);
+  hipError_t e = partial ? sa::launch_decode_stream(a, head_dim, sp, ra, nullptr, (hipStream_t)stream)
+                         : sa::launch_merge_stream(a, head_dim, sp, rows, false, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e);
   return SINK_ATTN_OK;
 }

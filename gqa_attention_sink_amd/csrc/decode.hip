@@ -29,17 +29,6 @@ __device__ __forceinline__ int plan_chunks(int lk, int num_splits, int cw) {
   const int n = (((lk + 255) >> 8) + cw - 1) / cw * cw;
   return min(16, max(4, n));
 }
-// Paged sequence b: its first page-list entry and its length, clamped so that every
-// page-list read stays inside the list.
-__device__ __forceinline__ int page_begin(const DecodeArgs& a, int b) {
-  return (int)min<int64_t>(max(a.kv_page_indptr[b], 0), a.num_page_entries);
-}
-__device__ __forceinline__ int paged_len(const DecodeArgs& a, int b, int e0) {
-  const int np = (int)min<int64_t>(max(a.kv_page_indptr[b + 1], e0), a.num_page_entries) - e0;
-  if (np == 0) return 0;
-  const int last = min(max(a.kv_last_page_len[b], 1), a.page_size);
-  return (int)min<int64_t>((int64_t)(np - 1) * a.page_size + last, 1 << 24);
-}
 // Bounded views of K and V for the rows of page-list slot `ps_slot` of a paged sequence
 // that lie before key `ke` (<= the sequence length): page ids are read with scalar
 // loads and clamped to the cache, rows at or past ke read zeros.

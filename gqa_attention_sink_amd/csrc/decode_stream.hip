@@ -24,14 +24,33 @@
 
 namespace sa {
 
+// A wave-uniform int32 read through the scalar unit.  The paged bounds are read while
+// copies are in flight; as vector loads they would first wait for every copy.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+// Two such reads under one wait.
+__device__ __forceinline__ void sload2_i32(const int32_t* p0, const int32_t* p1, int& v0, int& v1) {
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(p0), "s"(p1)
+               : "memory");
+}
+
 constexpr int kStreamWaves = 4;  // wavefronts per workgroup (independent, no barriers)
 
 // The sequence bounds are a separate __restrict__ argument so that the compiler reads
 // them with scalar loads, which wait for no copy in flight (a struct field is read with
 // vector loads, and every such read would wait for all copies).
-template <int D>
+// PAGED: the token axis is the page list laid end to end (entry e holds tokens
+// [e*page_size, (e+1)*page_size)), so sequence b spans [first entry * page_size, + L_b);
+// kv_indptr is then the page-list indptr and last_len the last-page lengths.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
-    DecodeArgs a, const int32_t* __restrict__ kv_indptr, StreamPlan sp, RopeArgs rope) {
+    DecodeArgs a, const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ page_ids,
+    const int32_t* __restrict__ last_len, StreamPlan sp, RopeArgs rope) {
   constexpr int KS = D / 32;
   constexpr int DPL = D / 16;
   constexpr int ROW = D * 2;
@@ -67,10 +86,25 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
   const int M = a.q_len * G;
   const int B = sp.batch;
   const int S = sp.smax;
-  // sequence bounds clamped to the token axis (as seq_begin / seq_end)
-  auto sbeg = [&](int bb) { return (int)min<int64_t>(max(kv_indptr[bb], 0), a.total_kv); };
+  // sequence bounds clamped to the token axis (as seq_begin / seq_end, or page_begin /
+  // paged_len on the page-list axis)
+  auto sbeg = [&](int bb) {
+    if constexpr (PAGED)
+      return (int)(min<int64_t>(max(sload_i32(kv_indptr + bb), 0), a.num_page_entries) * a.page_size);
+    else
+      return (int)min<int64_t>(max(kv_indptr[bb], 0), a.total_kv);
+  };
   auto send = [&](int bb) {
-    return (int)min<int64_t>(max(kv_indptr[bb + 1], sbeg(bb)), a.total_kv);
+    if constexpr (PAGED) {
+      const int64_t e0 = min<int64_t>(max(sload_i32(kv_indptr + bb), 0), a.num_page_entries);
+      const int64_t np =
+          min<int64_t>(max<int64_t>(sload_i32(kv_indptr + bb + 1), e0), a.num_page_entries) - e0;
+      const int last = min(max(sload_i32(last_len + bb), 1), a.page_size);
+      const int64_t len = np > 0 ? min<int64_t>((np - 1) * a.page_size + last, 1 << 24) : 0;
+      return (int)(e0 * a.page_size + len);
+    } else {
+      return (int)min<int64_t>(max(kv_indptr[bb + 1], sbeg(bb)), a.total_kv);
+    }
   };
   const int row_t = l16 / G;
   const int row_h = g * G + (l16 - row_t * G);
@@ -88,18 +122,72 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, range_bytes);
   const int lead = c0 - t0;  // tokens of the range before the view
   unsigned char (*my)[2][SB] = sm.ring[w];
+  // PAGED: first sequence not ending before the half-stage being issued (monotone, since
+  // stages are issued in order), with its bounds kept in registers
+  int ib = 0, ib_s = 0, ib_e = 0;
   auto issue = [&](int st) {
     unsigned char* kbuf = my[st % NST][0];
     unsigned char* vbuf = my[st % NST][1];
+    if constexpr (PAGED) {
+      // Each 16-row half of the stage lies in one page (the range starts on a multiple of
+      // 32 and the page size is a multiple of 16): one bounded view per half, holding the
+      // rows before its sequence's end, so unused page slots and gaps read zeros.
+      const int ps = a.page_size;
+      int rows[2], ent[2], pid[2] = {0, 0};
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int p = i * 64 + lane;
-      const int row = p / CPR;
-      const int cc = p - row * CPR;
-      const int tok = st * STEP + row - lead;  // token relative to the view
-      const uint32_t rbase = tok >= 0 ? (uint32_t)tok * ROW : kNoRead;
-      dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
-      dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      for (int h = 0; h < 2; ++h) {
+        const int vt = __builtin_amdgcn_readfirstlane(t0 + st * STEP + 16 * h);
+        int bi = __builtin_amdgcn_readfirstlane(ib);
+        while (bi < B && ib_e <= vt) {  // next sequence (rare: once per sequence end)
+          ++bi;
+          if (bi < B) {
+            ib_s = sbeg(bi);
+            ib_e = send(bi);
+          }
+        }
+        ib = __builtin_amdgcn_readfirstlane(bi);
+        const int r = (ib < B && vt >= ib_s) ? min(ib_e - vt, 16) : 0;
+        rows[h] = __builtin_amdgcn_readfirstlane(r);
+        ent[h] = vt / ps;  // rows > 0: vt < ib_e <= num_page_entries * ps, in the list
+      }
+      if (rows[0] > 0 && rows[1] > 0) sload2_i32(page_ids + ent[0], page_ids + ent[1], pid[0], pid[1]);
+      else if (rows[0] > 0) pid[0] = sload_i32(page_ids + ent[0]);
+      else if (rows[1] > 0) pid[1] = sload_i32(page_ids + ent[1]);
+      __amdgpu_buffer_rsrc_t kh[2], vh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (rows[h] > 0) {
+          const int64_t pc = min<int64_t>(max<int64_t>(pid[h], 0), a.num_pages - 1);
+          const int vt = t0 + st * STEP + 16 * h;
+          const size_t base = (((size_t)pc * a.num_kv_heads + g) * ps + (vt - ent[h] * ps)) * D;
+          kh[h] = make_rsrc((const __bf16*)a.k + base, (uint32_t)rows[h] * ROW);
+          vh[h] = make_rsrc((const __bf16*)a.v + base, (uint32_t)rows[h] * ROW);
+        } else {
+          kh[h] = make_rsrc(a.k, 0u);
+          vh[h] = make_rsrc(a.v, 0u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int p = i * 64 + lane;
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const int h = (i * (64 / CPR)) / 16;  // every row of copy i lies in half h
+        const uint32_t rb = (uint32_t)(row - 16 * h) * ROW;
+        dma16_nt(kh[h], rb + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16_nt(vh[h], rb + (uint32_t)(cc * 16), vbuf + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int p = i * 64 + lane;
+        const int row = p / CPR;
+        const int cc = p - row * CPR;
+        const int tok = st * STEP + row - lead;  // token relative to the view
+        const uint32_t rbase = tok >= 0 ? (uint32_t)tok * ROW : kNoRead;
+        dma16_nt(kr, rbase + (uint32_t)((cc ^ dswz<D>(row)) * 16), kbuf + i * 1024);
+        dma16_nt(vr, rbase + (uint32_t)(cc * 16), vbuf + i * 1024);
+      }
     }
   };
   // Q tile of sequence bb (rows past M, or bb < 0, read nothing and land as zeros).
@@ -132,6 +220,13 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
     const int mid = (lo + hi) >> 1;
     if (send(mid) <= t0) lo = mid + 1;
     else hi = mid;
+  }
+  ib = lo;
+  if constexpr (PAGED) {
+    if (lo < B) {
+      ib_s = sbeg(lo);
+      ib_e = send(lo);
+    }
   }
   int b = next_seq(lo);
   bool have = b < B && sbeg(b) < t1;
@@ -563,7 +658,7 @@ __global__ __launch_bounds__(64 * W) void decode_stream_wg_kernel(
 // sink[h].  D/4 lanes per row, four consecutive head dims each.  All of a row's loads
 // (at most kStreamMaxSlots slots, read once: non-temporal) are issued together, so a row
 // waits for one memory latency, not one per slot.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamPlan sp,
                                                            int64_t rows) {
   constexpr int LPR = D / 4;
@@ -587,7 +682,15 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
   for (int c = 0; c < kStreamMaxSlots; ++c)
     x[c] = (c < S) ? __builtin_nontemporal_load(po + (size_t)c * (D / 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
   const float sink = (a.sinks != nullptr) ? a.sinks[h] : kNegInf;
-  const int s0 = seq_begin(a, b), e0 = seq_end(a, b);
+  int s0, e0;
+  if constexpr (PAGED) {  // the sequence's extent on the page-list axis
+    const int ep = page_begin(a, b);
+    s0 = ep * a.page_size;
+    e0 = s0 + paged_len(a, b, ep);
+  } else {
+    s0 = seq_begin(a, b);
+    e0 = seq_end(a, b);
+  }
   const int n = (e0 > s0) ? min(S, (e0 - 1) / sp.R - s0 / sp.R + 1) : 0;
 #pragma unroll
   for (int c = 0; c < kStreamMaxSlots; ++c) {
@@ -625,7 +728,8 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
 }
 
 hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
-                                const RopeArgs& rope, hipStream_t stream) {
+                                const RopeArgs& rope, const int32_t* page_ids, hipStream_t stream) {
+  if (page_ids != nullptr && sp.waves > 1) return hipErrorInvalidValue;  // single-wavefront plan only
   if (sp.waves > 1) {  // one workgroup of sp.waves wavefronts per range
     const dim3 grid((unsigned)(sp.num_kv_heads * sp.nph));
     if (head_dim == 64) {
@@ -643,23 +747,34 @@ hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamP
   }
   const int waves = sp.num_kv_heads * sp.nph;
   const dim3 grid((unsigned)((waves + kStreamWaves - 1) / kStreamWaves));
-  if (head_dim == 64)
-    hipLaunchKernelGGL(decode_stream_kernel<64>, grid, dim3(64 * kStreamWaves), 0, stream, a,
-                       a.kv_indptr, sp, rope);
-  else
-    hipLaunchKernelGGL(decode_stream_kernel<128>, grid, dim3(64 * kStreamWaves), 0, stream, a,
-                       a.kv_indptr, sp, rope);
+  const dim3 block(64 * kStreamWaves);
+  if (page_ids != nullptr) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((decode_stream_kernel<64, true>), grid, block, 0, stream, a,
+                         a.kv_page_indptr, page_ids, a.kv_last_page_len, sp, rope);
+    else
+      hipLaunchKernelGGL((decode_stream_kernel<128, true>), grid, block, 0, stream, a,
+                         a.kv_page_indptr, page_ids, a.kv_last_page_len, sp, rope);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL((decode_stream_kernel<64, false>), grid, block, 0, stream, a, a.kv_indptr,
+                       nullptr, nullptr, sp, rope);
+  } else {
+    hipLaunchKernelGGL((decode_stream_kernel<128, false>), grid, block, 0, stream, a, a.kv_indptr,
+                       nullptr, nullptr, sp, rope);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_merge_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
-                               int64_t rows, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(merge_stream_kernel<64>, dim3((unsigned)((rows + 7) / 8)), dim3(128), 0,
-                       stream, a, sp, rows);
-  else
-    hipLaunchKernelGGL(merge_stream_kernel<128>, dim3((unsigned)((rows + 3) / 4)), dim3(128), 0,
-                       stream, a, sp, rows);
+                               int64_t rows, bool paged, hipStream_t stream) {
+  const dim3 g64((unsigned)((rows + 7) / 8)), g128((unsigned)((rows + 3) / 4));
+  if (head_dim == 64) {
+    if (paged) hipLaunchKernelGGL((merge_stream_kernel<64, true>), g64, dim3(128), 0, stream, a, sp, rows);
+    else hipLaunchKernelGGL((merge_stream_kernel<64, false>), g64, dim3(128), 0, stream, a, sp, rows);
+  } else {
+    if (paged) hipLaunchKernelGGL((merge_stream_kernel<128, true>), g128, dim3(128), 0, stream, a, sp, rows);
+    else hipLaunchKernelGGL((merge_stream_kernel<128, false>), g128, dim3(128), 0, stream, a, sp, rows);
+  }
   return hipGetLastError();
 }
 

@@ -124,10 +124,12 @@ hipError_t launch_rope_apply(void* x, int64_t tokens, int heads, int head_dim,
                              const int32_t* positions, const RopeArgs& rope, hipStream_t stream);
 // Stream decode (contiguous K/V, q_len * G <= 64): partials into a.part_o / a.part_lse,
 // then their merge with the sinks into a.out / a.lse.
+// page_ids: NULL for the contiguous cache, else the page list of a paged cache (the plan
+// must then be a single-wavefront plan over the page-list axis).
 hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
-                                const RopeArgs& rope, hipStream_t stream);
+                                const RopeArgs& rope, const int32_t* page_ids, hipStream_t stream);
 hipError_t launch_merge_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
-                               int64_t rows, hipStream_t stream);
+                               int64_t rows, bool paged, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows,
                         int num_slots, int head_dim, void* out, float* lse,
                         hipStream_t stream);

@@ -120,18 +120,35 @@ def test_paged_unused_slots_do_not_leak(sa):
 
 
 def test_paged_equals_contiguous_kernel_bitwise(sa):
-    """With the same chunk plan the paged and contiguous kernels combine the same keys in
-    the same order: identical results.  (Contiguous decode in planner mode takes the
-    stream plan here, so the contiguous side runs the chunk plan's two steps.)"""
+    """With the same chunk plan (4 chunks forced on both sides) the paged and contiguous
+    chunk kernels combine the same keys in the same order: identical results."""
     w = wl.make_decode([700, 3000, 64, 1], 1, 64, 8, 64, ("normal", 0, 2), 0.125, True, 0,
                        seed=620, device="cuda")
     pk = wl.make_paged(w, 64, seed=621)
-    _say("paged vs contiguous kernels")
-    op, lp = _run(sa, w, pk)
+    _say("paged vs contiguous chunk kernels")
+    op, lp = _run(sa, w, pk, ns=4)
     po, pl = sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
-                               w.causal, 0)
+                               w.causal, 4)
     oc, lc = sa.merge(po, pl)
     torch.cuda.synchronize()
+    assert torch.equal(op.reshape(oc.shape), oc) and torch.equal(lp.reshape(lc.shape), lc)
+
+
+@pytest.mark.parametrize("ps,d,ql,hq,hkv", [(16, 64, 1, 64, 8), (32, 128, 2, 16, 4)])
+def test_paged_stream_equals_contiguous_stream_bitwise(sa, ps, d, ql, hq, hkv):
+    """Sequence lengths that are multiples of the page size make the page list, laid end
+    to end, the same token axis as the contiguous cache: the stream plan, its ranges and
+    the order of every sum are then the same, so paged and contiguous decode agree bit
+    for bit although the pages are scattered."""
+    lens = [704, 3008, ps, 4 * ps, 1536]
+    w = wl.make_decode(lens, ql, hq, hkv, d, ("normal", 0, 2), 1 / math.sqrt(d), True, 0,
+                       seed=630 + ps, device="cuda")
+    pk = wl.make_paged(w, ps, seed=631 + ps, fill="nan")
+    _say(f"paged vs contiguous stream decode ps={ps} d={d}")
+    op, lp = _run(sa, w, pk)
+    oc, lc = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(op.float()).all()
     assert torch.equal(op.reshape(oc.shape), oc) and torch.equal(lp.reshape(lc.shape), lc)
 
 

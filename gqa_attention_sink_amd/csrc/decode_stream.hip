@@ -233,6 +233,15 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
   int bn = have ? next_seq(b + 1) : B;
   bool have_n = bn < B && sbeg(bn) < t1;
   int kseg = 0;  // index of the current segment (its Q tile sits in buffer kseg & 1)
+  // D=64: the YaRN frequencies of the lane's dims, read once before any copy goes out
+  // (read at each segment start they would wait for every copy in flight)
+  double rfreq[8];
+  if constexpr (D == 64) {
+    if (rope.enabled) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rfreq[j] = rope.freq[cg * 8 + j];
+    }
+  }
   issue_q(have ? b : -1, 0);
   issue_q(have_n ? bn : -1, 1);
 #pragma unroll
@@ -252,8 +261,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(
     const int s0 = sbeg(b), e0 = send(b);
     if (rope.enabled) {  // YaRN rotation of the query row at position Lk - q_len + t
       const int64_t pos = (int64_t)(e0 - s0) - a.q_len + row_t;
+      if constexpr (D == 64) {
+        rope_rotate8_f(qop[0], qop[1], rfreq, pos, rope.mscale);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
+        for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
+      }
     }
     sb = max(t0, s0);
     se = min(t1, e0);

@@ -47,17 +47,18 @@ __device__ __forceinline__ void rope_rotate8_cs(bf16x8& lo, bf16x8& hi, const fl
 }
 
 // Rotate eight half-split pairs held as two bf16 vectors: lo = dims [i0, i0+8),
-// hi = dims [i0 + D/2, i0 + D/2 + 8), at one position; results rounded to bf16 (RNE).
-__device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int i0, int64_t pos,
-                                             const RopeArgs& r) {
+// hi = dims [i0 + D/2, i0 + D/2 + 8), whose frequencies are f[0..8), at one position;
+// results rounded to bf16 (RNE).
+__device__ __forceinline__ void rope_rotate8_f(bf16x8& lo, bf16x8& hi, const double* f,
+                                               int64_t pos, float mscale) {
   float x[8], y[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float c, s;
-    rope_cos_sin(r.freq[i0 + j], pos, c, s);
+    rope_cos_sin(f[j], pos, c, s);
     const float a = (float)lo[j], b = (float)hi[j];
-    x[j] = r.mscale * (a * c - b * s);
-    y[j] = r.mscale * (b * c + a * s);
+    x[j] = mscale * (a * c - b * s);
+    y[j] = mscale * (b * c + a * s);
   }
   u32x4 xl, yl;
   xl.x = pack_bf16x2(x[0], x[1]); xl.y = pack_bf16x2(x[2], x[3]);
@@ -66,6 +67,14 @@ __device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int i0, int
   yl.z = pack_bf16x2(y[4], y[5]); yl.w = pack_bf16x2(y[6], y[7]);
   lo = as_bf16x8(xl);
   hi = as_bf16x8(yl);
+}
+// The same with the frequencies read from the table of `r`.
+__device__ __forceinline__ void rope_rotate8(bf16x8& lo, bf16x8& hi, int i0, int64_t pos,
+                                             const RopeArgs& r) {
+  double f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = r.freq[i0 + j];
+  rope_rotate8_f(lo, hi, f, pos, r.mscale);
 }
 
 }  // namespace sa

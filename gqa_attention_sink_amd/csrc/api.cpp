@@ -1,13 +1,16 @@
 // C ABI of libsinkattn: argument validation, planning and launch.  Every
 // host-checkable precondition is checked before the first HIP call; no C++ exception
-// crosses the boundary.
+// crosses the boundary.  Plain host C++: the kernels are reached only through the
+// launch layer (sa_launch.h), so this file also builds with a host compiler against a
+// stub of that layer (the sanitizer build).
 #include <math.h>
 #include <stdint.h>
 
 #include <new>
 
 #include "../../include/sink_attn.h"
-#include "sa_kernels.h"
+#include "sa_launch.h"
+#include "sa_plan.h"
 
 namespace {
 
@@ -26,14 +29,18 @@ inline bool dim_ok(int d) { return d == 64 || d == 128; }
 
 inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-// Largest chunk count of the decode plan (the device applies the same rule per
-// sequence): num_splits > 0 forces it; otherwise ceil(Lk/256) rounded up to a multiple of
-// cw (chunks per workgroup) and clamped to [4, 16].
+// Largest chunk count of the decode plan: the kernels apply the same rule
+// (sa::plan_chunks) to each sequence, and it is nondecreasing in the length.
 inline int planned_chunks(int32_t max_kv_len, int32_t num_splits, int cw) {
-  if (num_splits > 0) return num_splits;
-  int n = (int)((max_kv_len + 255) / 256);
-  n = (n + cw - 1) / cw * cw;
-  return n < 4 ? 4 : (n > 16 ? 16 : n);
+  return sa::plan_chunks(max_kv_len, num_splits, cw);
+}
+
+// Compute units the planners size grids for: the caller's count if positive, else the
+// current device's (read once per device), else 256 (MI355X) when no device is current.
+inline int resolve_cus(int32_t num_cus) {
+  if (num_cus > 0) return num_cus;
+  const int c = sa::device_cu_count();
+  return c > 0 ? c : 256;
 }
 
 // Partial slots per row: one per group of cw consecutive chunks.
@@ -51,8 +58,8 @@ inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
 // wavefronts (16 rows each) sharing each range.  R is at least max_kv/16 (so a sequence
 // overlaps at most 17 ranges, the slots a row needs) and a multiple of 32.
 using sa::kStreamMaxSlots;
-constexpr int kStreamWavesTotal = 4 * 256;
-constexpr int kStreamGroupsTotal = 2 * 256;
+constexpr int kStreamWavesPerCu = 4;
+constexpr int kStreamGroupsPerCu = 2;
 inline bool stream_eligible(int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
                             int32_t max_kv_len, int32_t num_splits) {
   return num_splits == 0 && q_len * (hq / hkv) <= 64 &&
@@ -60,11 +67,11 @@ inline bool stream_eligible(int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
 }
 inline int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
 sa::StreamPlan stream_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv,
-                           int64_t total_kv, int32_t max_kv_len) {
+                           int64_t total_kv, int32_t max_kv_len, int cus) {
   sa::StreamPlan p{};
   const int rows = q_len * (hq / hkv);
   p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  const int total = p.waves == 1 ? kStreamWavesTotal : kStreamGroupsTotal;
+  const int total = cus * (p.waves == 1 ? kStreamWavesPerCu : kStreamGroupsPerCu);
   p.nph = total / hkv > 0 ? total / hkv : 1;
   int64_t r = round32((total_kv + p.nph - 1) / p.nph);
   const int64_t r_floor = round32((max_kv_len + kStreamMaxSlots - 2) / (kStreamMaxSlots - 1));
@@ -87,16 +94,17 @@ inline size_t partial_bytes(int64_t rows, int64_t slots, int d) {
 // Key-axis splits of a prefill: num_splits > 0 forces them; 0 splits only when the
 // (head group, sequence, query tile) grid would leave the GPU under-filled (fewer than
 // four 8-wavefront workgroups per CU), keeping at least 8 key units (512 keys) per split.
-constexpr int kPrefillTargetWgs = 4 * 256;
+constexpr int kPrefillWgsPerCu = 4;
 int heads_per_wg(int group);
 int prefill_splits(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,
-                   int32_t num_splits) {
+                   int32_t num_splits, int cus) {
   if (num_splits > 0) return num_splits;
+  const int64_t target = (int64_t)kPrefillWgsPerCu * cus;
   const int group = hq / hkv;
   const int hg = heads_per_wg(group);
   const int64_t qtiles = (max_q + 32 * (8 / hg) - 1) / (32 * (8 / hg));
   const int64_t base = (int64_t)hkv * (group / hg) * batch * (qtiles > 0 ? qtiles : 1);
-  int64_t s = (kPrefillTargetWgs + base - 1) / base;
+  int64_t s = (target + base - 1) / base;
   const int64_t units = (max_kv + 63) / 64;
   if (s > units / 8) s = units / 8;
   if (s > 16) s = 16;
@@ -199,7 +207,8 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
                                                          head_dim, max_kv_len, num_splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
       return SINK_ATTN_ERR_WORKSPACE;
-    const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, axis, max_kv_len);
+    const sa::StreamPlan sp =
+        stream_plan(batch, q_len, num_q_heads, num_kv_heads, axis, max_kv_len, resolve_cus(0));
     a.total_kv = axis;
     const int64_t rows = (int64_t)batch * q_len * num_q_heads;
     a.part_o = (float*)workspace;
@@ -233,6 +242,23 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
   e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
   if (e != hipSuccess) return hip_fail(e);
   return SINK_ATTN_OK;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Rows of d elements at t*ts + h*hs (t < nt, h < nh) are pairwise disjoint when the
+// layout nests: the smaller stride (of an axis with more than one index) is at least d
+// and the larger is at least the smaller's extent.  Covers token-major [T, H, D] and
+// head-major [H, T, D]; other overlapping-free layouts are rejected too (conservative).
+inline bool rows_disjoint(int64_t nt, int64_t ts, int64_t nh, int64_t hs, int64_t d) {
+  int64_t n1 = nt, s1 = ts, n2 = nh, s2 = hs;
+  if (n1 <= 1) { n1 = 1; s1 = 0; }
+  if (n2 <= 1) { n2 = 1; s2 = 0; }
+  if (n1 == 1 && n2 == 1) return true;
+  if (n1 == 1) return s2 >= d;
+  if (n2 == 1) return s1 >= d;
+  if (s1 > s2) { const int64_t tn = n1, tsd = s1; n1 = n2; s1 = s2; n2 = tn; s2 = tsd; }
+  return s1 >= d && s2 / n1 >= s1;
 }
 
 // Paged caches: page_size a multiple of 16 (a 32-key stage then spans at most two pages
@@ -305,7 +331,7 @@ static int prefill_common(const void* q, const void* k, const void* v, const flo
   a.out = out;
   a.lse = lse;
   const int S = prefill_splits(batch, max_seqlen_q, max_seqlen_kv, num_q_heads, num_kv_heads,
-                               num_splits);
+                               num_splits, resolve_cus(0));
   const int units = (max_seqlen_kv + 63) / 64;
   a.num_splits = S;
   a.split_units = S > 1 ? (units + S - 1) / S : 0x7fffffff / 64;
@@ -348,12 +374,13 @@ int sink_attn_prefill(const void* q, const void* k, const void* v, const float* 
 
 int32_t sink_attn_prefill_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                                      int32_t num_q_heads, int32_t num_kv_heads,
-                                     int32_t num_splits) {
+                                     int32_t num_splits, int32_t num_cus) {
   if (batch < 1 || max_seqlen_q < 0 || max_seqlen_kv < 0 || num_q_heads < 1 ||
       num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 || num_splits < 0 ||
-      num_splits > kMaxSplits)
+      num_splits > kMaxSplits || num_cus < 0)
     return 0;
-  return prefill_splits(batch, max_seqlen_q, max_seqlen_kv, num_q_heads, num_kv_heads, num_splits);
+  return prefill_splits(batch, max_seqlen_q, max_seqlen_kv, num_q_heads, num_kv_heads, num_splits,
+                        resolve_cus(num_cus));
 }
 
 size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, int32_t head_dim,
@@ -395,6 +422,22 @@ int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim) {
   if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim)) return 0;
   return chunk_waves(q_len, num_q_heads, num_kv_heads, head_dim);
+}
+
+int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
+                                      int32_t* bounds, int32_t capacity) {
+  if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || kv_len < 0 ||
+      num_splits < 0 || num_splits > kMaxSplits || capacity < 0 || (capacity > 0 && !bounds))
+    return 0;
+  const int n = sa::plan_chunks(kv_len, num_splits, chunk_waves(q_len, num_q_heads, num_kv_heads,
+                                                                head_dim));
+  const int cl = sa::chunk_len(kv_len, n);
+  for (int c = 0; c <= n && c < capacity; ++c) {
+    const int64_t a = (int64_t)c * cl;
+    bounds[c] = (c == n || a > kv_len) ? kv_len : (int32_t)a;
+  }
+  return n;
 }
 
 int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
@@ -453,13 +496,14 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
 
 int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
-                                     int32_t max_kv_len, int32_t* range_tokens,
+                                     int32_t max_kv_len, int32_t num_cus, int32_t* range_tokens,
                                      int32_t* ranges_per_head, int32_t* slots) {
   if (batch < 1 || !slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || total_kv < 0 ||
-      total_kv > INT32_MAX || max_kv_len < 0 ||
+      total_kv > INT32_MAX || max_kv_len < 0 || num_cus < 0 ||
       !stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0))
     return 0;
-  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len);
+  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv,
+                                        max_kv_len, resolve_cus(num_cus));
   if (range_tokens) *range_tokens = sp.R;
   if (ranges_per_head) *ranges_per_head = sp.nph;
   if (slots) *slots = sp.smax;
@@ -488,7 +532,8 @@ static int stream_step(bool partial, const void* q, const void* k, const void* v
                                  num_q_heads, num_kv_heads, head_dim, sm_scale, causal, 0);
   sa::RopeArgs ra;
   if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
-  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len);
+  const sa::StreamPlan sp = stream_plan(batch, q_len, num_q_heads, num_kv_heads, total_kv,
+                                        max_kv_len, resolve_cus(0));
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + ((rows * sp.smax * head_dim * 4 + 255) & ~(int64_t)255));
@@ -606,6 +651,9 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* app
       return SINK_ATTN_ERR_INVALID_ARG;
     if (!page_size_ok(page_size) || !dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    // the copies are 16-byte vector accesses
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+      return SINK_ATTN_ERR_INVALID_ARG;
     sa::RopeArgs ra;
     if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
     if (max_append_len == 0 || total_new == 0) return SINK_ATTN_OK;
@@ -638,8 +686,11 @@ int sink_attn_rope_apply(void* x, int64_t num_tokens, int32_t num_heads, int32_t
     if (!x || !positions || !rope || num_tokens < 0 || num_heads < 1) return SINK_ATTN_ERR_INVALID_ARG;
     if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
     if (token_stride < 0 || head_stride < 0 || (token_stride % 8) != 0 || (head_stride % 8) != 0 ||
-        ((uintptr_t)x & 15u) != 0)
+        !aligned16(x))
       return SINK_ATTN_ERR_INVALID_ARG;  // 16-byte vector access
+    // in place: two (token, head) rows that overlap would be rotated by racing lanes
+    if (!rows_disjoint(num_tokens, token_stride, num_heads, head_stride, head_dim))
+      return SINK_ATTN_ERR_INVALID_ARG;
     if (num_tokens * num_heads * (head_dim / 16) > ((int64_t)1 << 38)) return SINK_ATTN_ERR_UNSUPPORTED;
     sa::RopeArgs ra;
     if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;

@@ -20,15 +20,6 @@
 
 namespace sa {
 
-// Split planner: chunk count of a sequence with lk keys and the chunk's key range.
-// num_splits > 0 forces that many chunks; 0 picks ceil(lk/256) rounded up to a multiple
-// of cw (the chunks one workgroup takes together) and clamped to [4, 16].  Every chunk
-// spans the same 32-key-aligned length, so trailing chunks may be empty.
-__device__ __forceinline__ int plan_chunks(int lk, int num_splits, int cw) {
-  if (num_splits > 0) return num_splits;
-  const int n = (((lk + 255) >> 8) + cw - 1) / cw * cw;
-  return min(16, max(4, n));
-}
 // Bounded views of K and V for the rows of page-list slot `ps_slot` of a paged sequence
 // that lie before key `ke` (<= the sequence length): page ids are read with scalar
 // loads and clamped to the cache, rows at or past ke read zeros.
@@ -50,13 +41,6 @@ __device__ __forceinline__ void page_views(const DecodeArgs& a, const int32_t* _
   kr = make_rsrc((const __bf16*)a.k + base, (uint32_t)rows * D * 2);
   vr = make_rsrc((const __bf16*)a.v + base, (uint32_t)rows * D * 2);
 }
-
-__device__ __forceinline__ int chunk_len(int lk, int n) {
-  int cl = lk > 0 ? (lk + n - 1) / n : 0;
-  return (cl + 31) & ~31;
-}
-
-
 
 // Decode split kernel.  Workgroup = W wavefronts = one (sequence, KV head, row group,
 // chunk); wavefront w owns 16 query rows.  The chunk's K and V stream from HBM into an

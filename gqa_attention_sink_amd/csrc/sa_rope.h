@@ -8,16 +8,9 @@
 #pragma once
 
 #include "sa_device.h"
+#include "sa_launch.h"
 
 namespace sa {
-
-constexpr int kMaxRopePairs = 64;  // head_dim <= 128
-
-struct RopeArgs {
-  double freq[kMaxRopePairs];  // radians per position of pair i (after YaRN interpolation)
-  float mscale;                // attention temperature factor, applied to q and to k
-  int32_t enabled;             // 0: no rotation
-};
 
 __device__ __forceinline__ void rope_cos_sin(double f, int64_t pos, float& c, float& s) {
   const double a = (double)pos * f;

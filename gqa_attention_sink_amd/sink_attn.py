@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
+# SINK_ATTN_LIB may name another build of the same C ABI (the host-sanitized build that
+# the CPU validation tests load); by default the in-tree HIP library.
+LIB_PATH = os.environ.get("SINK_ATTN_LIB") or os.path.join(_HERE, "libsinkattn.so")
 
 _lib = None
 
@@ -89,8 +91,11 @@ _SIGS["sink_attn_prefill_split"] = (ctypes.c_int, [
     ctypes.c_void_p, _ROPE_P, ctypes.c_void_p])
 _SIGS["sink_attn_decode_stream_plan"] = (ctypes.c_int32, [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-    ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)])
+_SIGS["sink_attn_decode_chunk_bounds"] = (ctypes.c_int32, [
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32])
 _SIGS["sink_attn_decode_stream_partial"] = (ctypes.c_int, [
     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
     ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -100,7 +105,7 @@ _SIGS["sink_attn_decode_stream_merge"] = (ctypes.c_int, [
     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
     ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p])
-_SIGS["sink_attn_prefill_num_splits"] = (ctypes.c_int32, [ctypes.c_int32] * 6)
+_SIGS["sink_attn_prefill_num_splits"] = (ctypes.c_int32, [ctypes.c_int32] * 7)
 _SIGS["sink_attn_prefill_workspace_bytes"] = (ctypes.c_size_t, [
     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32])
 _SIGS["sink_attn_rope_apply"] = (ctypes.c_int, [
@@ -235,9 +240,11 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
 
 
 def prefill_num_splits(batch: int, max_seqlen_q: int, max_seqlen_kv: int, num_q_heads: int,
-                       num_kv_heads: int, num_splits: int = 0) -> int:
+                       num_kv_heads: int, num_splits: int = 0, num_cus: int = 0) -> int:
+    """Resolved key-split count; num_cus = 0 plans for the current device."""
     return int(load().sink_attn_prefill_num_splits(batch, int(max_seqlen_q), int(max_seqlen_kv),
-                                                   num_q_heads, num_kv_heads, int(num_splits)))
+                                                   num_q_heads, num_kv_heads, int(num_splits),
+                                                   int(num_cus)))
 
 
 def prefill_workspace_bytes(total_q: int, num_q_heads: int, head_dim: int, splits: int) -> int:
@@ -248,6 +255,21 @@ def prefill_workspace_bytes(total_q: int, num_q_heads: int, head_dim: int, split
 def decode_chunks_per_slot(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
     """Consecutive plan chunks whose merged state one partial slot holds."""
     return int(load().sink_attn_decode_chunks_per_slot(q_len, num_q_heads, num_kv_heads, head_dim))
+
+
+def decode_chunk_bounds(kv_len: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                        head_dim: int, num_splits: int = 0) -> list:
+    """Boundaries [0, ..., kv_len] of the decode chunk plan of one sequence (chunk c
+    covers keys [b[c], b[c+1]))."""
+    lib = load()
+    n = int(lib.sink_attn_decode_chunk_bounds(int(kv_len), q_len, num_q_heads, num_kv_heads,
+                                              head_dim, int(num_splits), None, 0))
+    if n == 0:
+        raise SinkAttnError("invalid arguments for the decode chunk plan")
+    buf = (ctypes.c_int32 * (n + 1))()
+    lib.sink_attn_decode_chunk_bounds(int(kv_len), q_len, num_q_heads, num_kv_heads, head_dim,
+                                      int(num_splits), buf, n + 1)
+    return list(buf)
 
 
 def decode_num_slots(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -345,13 +367,13 @@ def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optiona
 
 
 def decode_stream_plan(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
-                       head_dim: int, total_kv: int, max_kv_len: int):
+                       head_dim: int, total_kv: int, max_kv_len: int, num_cus: int = 0):
     """(R, ranges_per_head, slots) of the stream plan decode() uses for these sizes, or
-    None when it uses the chunk plan."""
+    None when it uses the chunk plan.  num_cus = 0 plans for the current device."""
     r, n, s = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     ok = load().sink_attn_decode_stream_plan(batch, q_len, num_q_heads, num_kv_heads, head_dim,
-                                             int(total_kv), int(max_kv_len), ctypes.byref(r),
-                                             ctypes.byref(n), ctypes.byref(s))
+                                             int(total_kv), int(max_kv_len), int(num_cus),
+                                             ctypes.byref(r), ctypes.byref(n), ctypes.byref(s))
     return (r.value, n.value, s.value) if ok else None
 
 

@@ -31,7 +31,9 @@
  *    offsets within the totals) are documented, not checked, because checking them
  *    would need a synchronisation -- but every device read of K, V and Q goes through
  *    bounded buffer loads, so a violation yields wrong numbers, never a fault.
- *  - Thread-safe; no global mutable state beyond a per-thread last-HIP-error slot.
+ *  - Thread-safe; no global mutable state beyond a per-thread last-HIP-error slot and
+ *    the compute-unit count of each device, read once per device (std::call_once) the
+ *    first time a plan is made with it current.
  */
 #ifndef SINK_ATTN_H
 #define SINK_ATTN_H
@@ -123,11 +125,12 @@ int sink_attn_prefill_split(const void* q, const void* k, const void* v, const f
                             const sink_attn_rope* rope, void* stream);
 
 /* Resolved split count of sink_attn_prefill_split (0 if the arguments are invalid): with
- * num_splits = 0, enough splits for about four workgroups per CU, at most 16, each of at
- * least 512 keys. */
+ * num_splits = 0, enough splits for about four workgroups per compute unit, at most 16,
+ * each of at least 512 keys.  num_cus: compute units to plan for; 0 = those of the
+ * current device (what sink_attn_prefill_split uses), or 256 when no device is current. */
 int32_t sink_attn_prefill_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                                      int32_t num_q_heads, int32_t num_kv_heads,
-                                     int32_t num_splits);
+                                     int32_t num_splits, int32_t num_cus);
 
 /* Workspace bytes of sink_attn_prefill_split for S resolved splits (0 when S = 1 or the
  * arguments are invalid). */
@@ -188,6 +191,15 @@ size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t nu
 int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim);
 
+/* Chunk plan of one sequence with kv_len keys ("Sink attention": blocks along the key
+ * axis; the pages fix no size): the number of chunks n (0 if the arguments are invalid)
+ * and, in bounds[0..min(n+1, capacity)), their boundaries: chunk c covers keys
+ * [bounds[c], bounds[c+1]), bounds[0] = 0, bounds[n] = kv_len.  The kernels derive the
+ * same plan on the device from each sequence's length (no plan is passed to them). */
+int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
+                                      int32_t* bounds, int32_t capacity);
+
 /* Partial slots per row the decode path uses (the S of the partial layout):
  * ceil(n_max / C) with n_max the planner's chunk count at max_kv_len.  0 if invalid. */
 int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
@@ -223,6 +235,9 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
  * sink_attn_decode_stream_plan: 1 if the stream plan applies to these sizes (then R, the
  *   ranges per head and the slots S per row are written where the pointers are not
  *   NULL), else 0.  R is a multiple of 32, at least ceil(max_kv_len/16), so S <= 17.
+ *   The plan gives about 4 wavefronts (<= 16 rows) or 2 workgroups per compute unit:
+ *   num_cus is the count to plan for, 0 = the current device's (what sink_attn_decode
+ *   uses), or 256 when no device is current.
  * sink_attn_decode_stream_partial: the first step on its own, into `workspace` (size and
  *   alignment as for sink_attn_decode): part_o fp32 [rows, S, head_dim] at offset 0,
  *   part_lse fp32 [rows, S] at the next 256-byte boundary, rows = batch*q_len*num_q_heads.
@@ -236,7 +251,7 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
  */
 int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
-                                     int32_t max_kv_len, int32_t* range_tokens,
+                                     int32_t max_kv_len, int32_t num_cus, int32_t* range_tokens,
                                      int32_t* ranges_per_head, int32_t* slots);
 int sink_attn_decode_stream_partial(const void* q, const void* k, const void* v,
                                     const int32_t* kv_indptr, int32_t batch, int32_t q_len,
@@ -306,6 +321,8 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
  *  be negative are skipped.  max_append_len: host upper bound of n_b.
  *  rope: NULL, or YaRN parameters: each new key is rotated at its position as it is
  *  written (values are copied unchanged).
+ *  k_new, v_new, k_cache and v_cache must be 16-byte aligned (the copies are 16-byte
+ *  vector accesses), else SINK_ATTN_ERR_INVALID_ARG.
  */
 int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* append_indptr,
                         const int32_t* kv_page_indptr, const int32_t* kv_page_indices,
@@ -319,7 +336,10 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, const int32_t* app
  * h < num_heads, d < head_dim, at x + t*token_stride + h*head_stride + d (strides in
  * elements, multiples of 8; x 16-byte aligned), token t at positions[t] (int32, device).
  * For example contiguous HND keys [Hkv, total, D] have token_stride D and head_stride
- * total*D.  rope must not be NULL. */
+ * total*D.  rope must not be NULL.  The rows must not overlap (they are rewritten in
+ * place): the smaller stride of an axis with more than one index must be at least
+ * head_dim and the larger at least the smaller axis's extent, as in [T, H, D] and
+ * [H, T, D] layouts; anything else is SINK_ATTN_ERR_INVALID_ARG. */
 int sink_attn_rope_apply(void* x, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
                          int64_t token_stride, int64_t head_stride, const int32_t* positions,
                          const sink_attn_rope* rope, void* stream);

@@ -228,7 +228,8 @@ def test_rope_validation(lib):
 
 
 def test_prefill_split_planner_and_validation(lib):
-    ns = lib.sink_attn_prefill_num_splits
+    def ns(*a):
+        return lib.sink_attn_prefill_num_splits(*a, 256)   # planned for 256 CUs
     # 1024 new tokens over 32768 keys, 64 query heads over 8: 16 head groups (4 heads each)
     # x 16 query tiles (64 positions) = 256 workgroups -> 4 splits for ~1024
     assert ns(1, 1024, 32768, 64, 8, 0) == 4
@@ -238,6 +239,7 @@ def test_prefill_split_planner_and_validation(lib):
     assert ns(1, 6000, 6000, 64, 4, 0) == 1           # a full prefill fills the GPU
     assert ns(1, 64, 100, 64, 8, 0) == 1 and ns(2, 64, 64, 8, 8, 5) == 5
     assert ns(0, 1, 1, 8, 8, 0) == 0 and ns(1, 1, 1, 8, 3, 0) == 0 and ns(1, 1, 1, 8, 8, 65) == 0
+    assert lib.sink_attn_prefill_num_splits(1, 1, 1, 8, 8, 0, -1) == 0
     wb = lib.sink_attn_prefill_workspace_bytes
     rows, s, d = 4096 * 64, 4, 64
     o = (rows * s * d * 4 + 255) // 256 * 256
@@ -252,3 +254,126 @@ def test_prefill_split_planner_and_validation(lib):
     assert call() == WORKSPACE                       # 4 splits need a workspace
     assert call(ns=-1) == INVALID and call(ns=65) == INVALID and call(maxkv=-1) == INVALID
     assert call(d=80) == UNSUPPORTED
+
+
+# ---------------------------------------------------------------- plans sized by CUs
+@pytest.mark.parametrize("cus", [256, 80, 32])
+def test_prefill_splits_follow_cu_count(lib, cus):
+    """About four 8-wavefront workgroups per CU: the chunked-prefill grid (256
+    workgroups) is split until it reaches 4*cus, at most 16 splits of >= 512 keys."""
+    ns = lib.sink_attn_prefill_num_splits
+    base = 16 * 16                                     # head groups x query tiles
+    want = min(16, max(1, -(-4 * cus // base)), 32768 // 64 // 8)
+    assert ns(1, 1024, 32768, 64, 8, 0, cus) == want
+    assert ns(1, 6000, 6000, 64, 4, 0, cus) == 1     # already >= 4 per CU
+    assert ns(1, 1024, 32768, 64, 8, 3, cus) == 3    # forced
+
+
+@pytest.mark.parametrize("cus", [256, 80, 32])
+@pytest.mark.parametrize("b,ql,hq,hkv,d,total,maxkv,per_cu", [
+    (64, 1, 64, 8, 64, 294802, 8192, 4),      # <= 16 rows: ~4 wavefronts per CU
+    (256, 4, 64, 4, 128, 256 * 32768, 32768, 2),  # 64 rows: ~2 workgroups per CU
+])
+def test_stream_plan_follows_cu_count(lib, cus, b, ql, hq, hkv, d, total, maxkv, per_cu):
+    r, n, s = (sa.ctypes.c_int32(), sa.ctypes.c_int32(), sa.ctypes.c_int32())
+    ok = lib.sink_attn_decode_stream_plan(b, ql, hq, hkv, d, total, maxkv, cus,
+                                          sa.ctypes.byref(r), sa.ctypes.byref(n),
+                                          sa.ctypes.byref(s))
+    assert ok == 1
+    assert n.value == per_cu * cus // hkv               # ranges per KV head
+    assert r.value % 32 == 0 and n.value * r.value >= total
+    assert r.value >= -(-maxkv // 16) and s.value <= 17
+    # fewer CUs: longer ranges, never more work units than the device holds at once
+    assert n.value * hkv <= per_cu * cus
+    assert lib.sink_attn_decode_stream_plan(b, ql, hq, hkv, d, total, maxkv, -1, None, None,
+                                            None) == 0
+
+
+# ---------------------------------------------------------------- decode chunk plan
+def _bounds(lib, lk, ql, hq, hkv, d, ns):
+    n = lib.sink_attn_decode_chunk_bounds(lk, ql, hq, hkv, d, ns, None, 0)
+    buf = (sa.ctypes.c_int32 * (n + 1))()
+    assert lib.sink_attn_decode_chunk_bounds(lk, ql, hq, hkv, d, ns, buf, n + 1) == n
+    return list(buf)
+
+
+@pytest.mark.parametrize("ql,hq,hkv,d", [(1, 64, 8, 64), (4, 64, 4, 128), (2, 16, 4, 64),
+                                         (1, 64, 8, 128), (4, 32, 4, 64)])
+def test_decode_chunk_plan_is_a_partition(lib, ql, hq, hkv, d):
+    """The plan the kernels derive per sequence: a partition of [0, Lk) into equal
+    32-key-aligned chunks (trailing ones may be empty); the planner picks 4..16 chunks,
+    a multiple of the chunks one workgroup merges; a forced count is taken as given."""
+    cps = lib.sink_attn_decode_chunks_per_slot(ql, hq, hkv, d)
+    for lk in (0, 1, 31, 32, 33, 255, 256, 1000, 1024, 1025, 4097, 8192, 32768, 100000):
+        for ns in (0, 1, 3, 7, 32, 64):
+            b = _bounds(lib, lk, ql, hq, hkv, d, ns)
+            n = len(b) - 1
+            assert b[0] == 0 and b[-1] == lk and all(x <= y for x, y in zip(b, b[1:]))
+            lens = [y - x for x, y in zip(b, b[1:])]
+            # cuts inside the sequence sit on 32-key stage boundaries
+            assert all(x % 32 == 0 for x in b[:-1] if x < lk)
+            # non-empty chunks share one length (the last may be shorter), no longer than
+            # 32-key alignment forces: (len - 32) * n < lk
+            full = [x for x in lens if x > 0]
+            if len(full) > 1:
+                cl = full[0]
+                assert cl % 32 == 0 and all(x == cl for x in full[:-1]) and full[-1] <= cl
+                assert (cl - 32) * n < lk
+            assert all(x == 0 for x in lens[len(full):])      # empty chunks trail
+            if ns:
+                assert n == ns
+            else:
+                assert 4 <= n <= 16 and n % cps == 0
+                assert n >= min(16, -(-lk // 256))           # about 256 keys per chunk at most
+    # the gpt-oss decode lengths (1024..8192 keys, 8 rows per KV head, 4 chunks merged per
+    # workgroup) get 4..16 chunks, as that workload asks
+    if (ql, hq, hkv, d) == (1, 64, 8, 64):
+        for lk in (1024, 2048, 4096, 8192):
+            n = len(_bounds(lib, lk, ql, hq, hkv, d, 0)) - 1
+            assert 4 <= n <= 16
+    # the speculative decode's 32 chunks of 1024 keys
+    if (ql, hq, hkv, d) == (4, 64, 4, 128):
+        assert _bounds(lib, lk=32768, ql=4, hq=64, hkv=4, d=128, ns=32) == list(range(0, 32769, 1024))
+
+
+def test_decode_chunk_plan_rejects(lib):
+    f = lib.sink_attn_decode_chunk_bounds
+    assert f(-1, 1, 64, 8, 64, 0, None, 0) == 0 and f(10, 5, 64, 8, 64, 0, None, 0) == 0
+    assert f(10, 1, 64, 8, 80, 0, None, 0) == 0 and f(10, 1, 64, 8, 64, 65, None, 0) == 0
+    assert f(10, 1, 64, 8, 64, 0, None, 3) == 0       # capacity without a buffer
+    buf = (sa.ctypes.c_int32 * 3)(-7, -7, -7)
+    assert f(1000, 1, 64, 8, 64, 4, buf, 2) == 4      # only `capacity` entries written
+    assert list(buf) == [0, 256, -7]
+
+
+# ---------------------------------------------------------------- in-place rotation, append
+def test_rope_apply_rejects_overlapping_rows(lib):
+    R = sa.RopeParams
+    ra = lib.sink_attn_rope_apply
+    ok = sa.ctypes.byref(R(150000.0, 32.0, 4096, 32.0, 1.0))
+    def call(n, h, d, ts, hs):
+        return ra(FAKE, n, h, d, ts, hs, FAKE, ok, None)
+    # token-major [T, H, D] and head-major [H, T, D] are accepted: they pass validation
+    # and would launch (with no device that ends in a HIP error).  Never run with a
+    # device: the pointers are fake.
+    import torch
+    if not torch.cuda.is_available():
+        for args in ((4, 2, 64, 128, 64), (4, 2, 64, 64, 256), (1, 1, 64, 0, 0),
+                     (4, 1, 64, 64, 0), (1, 3, 128, 0, 128)):
+            assert call(*args) not in (INVALID, UNSUPPORTED), args
+    # rows that overlap: rotated twice by racing lanes -> rejected
+    for args in ((4, 2, 64, 0, 64), (4, 2, 64, 64, 0), (4, 2, 64, 32, 256), (1, 2, 64, 0, 32),
+                 (3, 1, 64, 8, 0), (4, 2, 64, 64, 128), (4, 4, 64, 128, 64)):
+        assert call(*args) == INVALID, args
+
+
+def test_kv_append_rejects_misaligned(lib):
+    ap = lib.sink_attn_kv_append
+    odd = sa.ctypes.c_void_p(0x1008)
+    def acall(**kw):
+        a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE)
+        a.update(kw)
+        return ap(a["kn"], a["vn"], FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 8, 8, 16, 2, 64, a["kc"],
+                  a["vc"], None, None)
+    for key in ("kn", "vn", "kc", "vc"):
+        assert acall(**{key: odd}) == INVALID, key

@@ -298,8 +298,10 @@ def test_decode_partials_match_oracle_chunks(sa, ns):
     assert cps == 4  # 8 rows per KV head: four chunks per slot
     bounds = []
     for lk in lens:
-        bd = oracle.plan_chunks(lk, ns, multiple=cps)
-        bd = bd[::cps] if (len(bd) - 1) % cps == 0 else bd[::cps] + [lk]  # slot = chunk group
+        # the library's own plan (its CPU tests check it is a valid partition); the oracle
+        # takes any bounds, so a slot is the group of cps consecutive plan chunks
+        bd = sa.decode_chunk_bounds(lk, 2, 16, 4, 64, ns)
+        bd = bd[::cps] if (len(bd) - 1) % cps == 0 else bd[::cps] + [lk]
         bounds.append(bd + [lk] * (s + 1 - len(bd)))
     cu_q = torch.arange(len(lens) + 1, dtype=torch.int32) * 2
     q2 = w.q.reshape(-1, 16, 64)

@@ -9,7 +9,6 @@ from .sink_attention import (  # noqa: F401
     sink_attention_decode,
     sink_attention_chunked,
     merge_partials,
-    plan_chunks,
     flops_causal,
 )
 from .paged_kv import (  # noqa: F401

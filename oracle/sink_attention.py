@@ -46,7 +46,6 @@ __all__ = [
     "sink_attention_decode",
     "sink_attention_chunked",
     "merge_partials",
-    "plan_chunks",
     "flops_causal",
 ]
 
@@ -173,27 +172,6 @@ def merge_partials(part_o, part_lse):
                        np.einsum("rs,rsd->rd", w, po) / np.where(dead, 1.0, wsum)[:, None])
         lse = np.where(dead, -np.inf, ms + np.log(np.where(dead, 1.0, wsum)))
     return out, lse
-
-
-def plan_chunks(lk: int, num_splits: int, tile: int = 32, multiple: int = 1) -> list[int]:
-    """Chunk boundaries [a_0=0, ..., a_n=lk] of one sequence's keys.
-
-    The pages split attention along the KV length into blocks ("Sink attention") and
-    parallelise over heads and KV length, but fix no block size.  Reading used here:
-    n = num_splits if num_splits > 0, else ceil(lk / 256) rounded up to a multiple of
-    ``multiple`` (chunks that are processed as one group) and clamped to [4, 16]; every
-    chunk has the same length, ceil(lk / n) rounded up to a multiple of ``tile``, so
-    trailing chunks may be empty.
-    """
-    if num_splits > 0:
-        n = num_splits
-    else:
-        n = -(-lk // 256)
-        n = -(-n // multiple) * multiple
-        n = min(16, max(4, n))
-    cl = -(-lk // n) if lk > 0 else 0
-    cl = -(-cl // tile) * tile
-    return [min(lk, c * cl) for c in range(n)] + [lk]
 
 
 def sink_attention_chunked(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, sm_scale: float,

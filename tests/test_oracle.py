@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (flops_causal, merge_partials, plan_chunks, sink_attention,
-                    sink_attention_chunked, sink_attention_decode)
+from oracle import (flops_causal, merge_partials, sink_attention, sink_attention_chunked,
+                    sink_attention_decode)
 from oracle.bruteforce import sink_attention_mp
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -191,22 +191,6 @@ def test_merge_handles_empty_chunks():
     np.testing.assert_allclose(out[1], [(3.0 + 3 * 5.0) / 4, (-1.0 + 3 * 1.0) / 4])
     assert abs(lse[1] - math.log(4.0)) < 1e-15
     assert np.all(out[2] == 0) and np.isneginf(lse[2])
-
-
-def test_plan_chunks_rule():
-    for lk in (1, 31, 32, 255, 256, 511, 512, 1024, 4097, 8192):
-        b = plan_chunks(lk, 0)
-        n = len(b) - 1
-        assert n == min(16, max(4, -(-lk // 256)))
-        assert b[0] == 0 and b[-1] == lk and all(x <= y for x, y in zip(b, b[1:]))
-        assert all(x % 32 == 0 or x == lk for x in b)
-    assert len(plan_chunks(1024, 0)) - 1 == 4 and len(plan_chunks(4096, 0)) - 1 == 16
-    assert plan_chunks(32768, 32) == list(range(0, 32768, 1024)) + [32768]
-    # grouped planning: the count is a multiple of the group size before the clamp
-    for lk, grp, want in ((1024, 4, 4), (1025, 4, 8), (3000, 4, 12), (9000, 4, 16),
-                          (100, 4, 4), (2049, 2, 10), (100, 2, 4), (5000, 2, 16)):
-        assert len(plan_chunks(lk, 0, multiple=grp)) - 1 == want
-    assert plan_chunks(777, 7, multiple=4) == plan_chunks(777, 7)
 
 
 # ---------------------------------------------------------------- P8 GQA == MHA

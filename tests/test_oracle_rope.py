@@ -81,3 +81,22 @@ def test_bf16_round_is_round_to_nearest_even():
     x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-3, 4, 100000)).astype(np.float32)
     want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
     assert np.array_equal(bf16_round(x.astype(np.float64)), want)
+
+
+def test_interpolation_band_golden():
+    """Hand-derived frequencies inside the YaRN band (tests/golden/yarn_midband.json):
+    the linear mix of f_i / s and f_i in the continuous turn count.  The fixture also
+    records what a wavelength blend and a ramp over rounded dimension indices give, and
+    those must be far from the expected values (so either misreading would fail)."""
+    import json
+    import os
+    data = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "yarn_midband.json")))
+    p = data["params"]
+    f = yarn_inv_freq(p["head_dim"], p["theta"], p["factor"], p["original_max_pos"],
+                      p["beta_fast"], p["beta_slow"])
+    for case in data["cases"]:
+        want = float(case["expected"])
+        got = f[case["pair"]]
+        assert abs(got - want) <= 1e-13 * want, (case["pair"], got, want)
+        for name, alt in case["not_this"].items():
+            assert abs(float(alt) - want) > 0.1 * want, name

@@ -8,7 +8,10 @@ from .sink_attn import (  # noqa: F401
     RopeParams,
     SinkAttnError,
     decode,
+    decode_chunk_bounds,
     decode_chunks_per_slot,
+    decode_noalloc,
+    decode_noalloc_scratch_bytes,
     decode_num_slots,
     decode_paged,
     decode_partial,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libsinkattn.so")
 HOST_SAN_LIB = os.path.join(PKG, "libsinkattn_host_asan.so")
 HOST_SOURCES = ["api.cpp"]
-HIP_SOURCES = ["runtime.hip", "prefill.hip", "decode.hip", "decode_stream.hip", "kv_append.hip"]
+HIP_SOURCES = ["runtime.hip", "noalloc.hip", "prefill.hip", "decode.hip", "decode_stream.hip", "kv_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_INCLUDE = "/opt/rocm/include"
 

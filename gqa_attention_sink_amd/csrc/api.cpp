@@ -278,6 +278,9 @@ const char* sink_attn_status_str(int status) {
     case SINK_ATTN_ERR_WORKSPACE: return "SINK_ATTN_ERR_WORKSPACE: workspace missing or too small";
     case SINK_ATTN_ERR_HIP: return "SINK_ATTN_ERR_HIP: a HIP call failed";
     case SINK_ATTN_ERR_INTERNAL: return "SINK_ATTN_ERR_INTERNAL: internal error";
+    case SINK_ATTN_ERR_SCRATCH_LIMIT:
+      return "SINK_ATTN_ERR_SCRATCH_LIMIT: the input needs more scratch than the no-allocation "
+             "entry point holds (sink_attn_decode_noalloc_scratch_bytes)";
     default: return "unknown sink_attn status";
   }
 }
@@ -598,6 +601,40 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
     return SINK_ATTN_ERR_INTERNAL;
   }
 }
+
+int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const float* sinks,
+                             const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                             int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                             int32_t causal, int32_t num_splits, void* out, float* lse,
+                             const sink_attn_rope* rope, void* stream) {
+  try {
+    int rc = check_decode_args(q, k, v, kv_indptr, batch, q_len, total_kv, max_kv_len,
+                               num_q_heads, num_kv_heads, head_dim, sm_scale, causal, num_splits);
+    if (rc != SINK_ATTN_OK) return rc;
+    if (!out) return SINK_ATTN_ERR_INVALID_ARG;
+    if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
+    sa::RopeArgs ra;
+    if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
+    // the workspace sink_attn_decode would need must fit the scratch array
+    if (sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                         max_kv_len, num_splits) > sa::kNoAllocScratchBytes)
+      return SINK_ATTN_ERR_SCRATCH_LIMIT;
+    void* scratch = nullptr;
+    const hipError_t e = sa::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+                                   num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
+                                   num_splits);
+    return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                      num_splits, nullptr, ra, scratch, sa::kNoAllocScratchBytes, out, lse,
+                      stream);
+  } catch (...) {
+    return SINK_ATTN_ERR_INTERNAL;
+  }
+}
+
+size_t sink_attn_decode_noalloc_scratch_bytes(void) { return sa::kNoAllocScratchBytes; }
 
 int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                            const float* sinks, const int32_t* kv_page_indptr,

@@ -8,6 +8,11 @@ namespace sa {
 
 int device_cu_count() { return 0; }
 
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  return hipErrorNoDevice;
+}
+
 hipError_t launch_prefill(const PrefillArgs&, int, int, const RopeArgs&, hipStream_t) {
   return hipErrorNoDevice;
 }

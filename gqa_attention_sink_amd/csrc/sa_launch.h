@@ -124,6 +124,12 @@ inline int decode_chunk_waves(int rows, int head_dim) {
 // current or the query fails).
 int device_cu_count();
 
+// The scratch array of the no-allocation decode entry point on the current device: its
+// device address, looked up once per device (the first call with that device current).
+// Returns the HIP error of reading the current device or of that lookup.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // rope: YaRN rotation of Q (and of new K in the append) at each row's position;
 // rope.enabled == 0 leaves them unrotated.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int num_kv_heads,

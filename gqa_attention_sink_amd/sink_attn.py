@@ -48,6 +48,12 @@ _SIGS = {  # entry points that take a rope pointer have it just before the strea
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p]),
+    "sink_attn_decode_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sink_attn_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "sink_attn_decode_partial": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -78,7 +84,8 @@ _SIGS = {  # entry points that take a rope pointer have it just before the strea
 }
 
 
-for _name in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_partial",
+for _name in ("sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_noalloc",
+              "sink_attn_decode_partial",
               "sink_attn_decode_paged", "sink_attn_kv_append"):
     _res, _args = _SIGS[_name]
     _SIGS[_name] = (_res, _args[:-1] + [_ROPE_P, _args[-1]])
@@ -336,6 +343,33 @@ def decode(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float]
                               _ptr(lse), _rope_arg(rope), _stream(q.device))
     _check(rc)
     return out, lse
+
+
+def decode_noalloc(q, k, v, sinks, kv_indptr, max_kv_len: int, out, lse=None,
+                   sm_scale: Optional[float] = None, causal: bool = True, num_splits: int = 0,
+                   rope: Optional[RopeParams] = None):
+    """decode() through the entry point that allocates nothing: the partials live in the
+    library's per-GPU scratch array (decode_noalloc_scratch_bytes() bytes), so `out`
+    (and `lse`, if wanted) must be given.  Calls that may overlap on one GPU race."""
+    lib = load()
+    b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
+    sinks = _sinks_arg(sinks, hq, q.device)
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _dev_tensor(out, torch.bfloat16, "out", 4)
+    _need(out.shape == q.shape, "out must match q")
+    if lse is not None:
+        _dev_tensor(lse, torch.float32, "lse", 3)
+        _need(tuple(lse.shape) == (b, ql, hq), "lse must be [B, q_len, Hq]")
+    rc = lib.sink_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(kv_indptr),
+                                      b, ql, tk, int(max_kv_len), hq, hkv, d, scale,
+                                      int(bool(causal)), int(num_splits), _ptr(out), _ptr(lse),
+                                      _rope_arg(rope), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return int(load().sink_attn_decode_noalloc_scratch_bytes())
 
 
 def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optional[float] = None,

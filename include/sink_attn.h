@@ -51,7 +51,8 @@ typedef enum {
   SINK_ATTN_ERR_UNSUPPORTED = 2,   /* valid but not instantiated (head_dim, q_len...) */
   SINK_ATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small                  */
   SINK_ATTN_ERR_HIP = 4,           /* a HIP call failed; see sink_attn_last_hip_error */
-  SINK_ATTN_ERR_INTERNAL = 5       /* unexpected internal failure                     */
+  SINK_ATTN_ERR_INTERNAL = 5,      /* unexpected internal failure                     */
+  SINK_ATTN_ERR_SCRATCH_LIMIT = 6  /* larger than the no-allocation entry point holds */
 } sink_attn_status;
 
 /*
@@ -176,6 +177,34 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
                      int32_t causal, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* out, float* lse,
                      const sink_attn_rope* rope, void* stream);
+
+/*
+ * sink_attn_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments, plan, kernels and results are those of sink_attn_decode; the
+ * partials live in a file-scope device array of the library instead of a caller's
+ * workspace.  Nothing is allocated or freed by the call.
+ *  - Limit: inputs whose sink_attn_decode_workspace_bytes(...) exceeds
+ *    sink_attn_decode_noalloc_scratch_bytes() (32 MiB) are rejected with
+ *    SINK_ATTN_ERR_SCRATCH_LIMIT before any HIP call.  (The gpt-oss-like batch of 64
+ *    sequences up to 8192 keys, 64 query heads over 8, fits; a 256-sequence
+ *    speculative-decode batch does not: use sink_attn_decode with a workspace.)
+ *  - Each GPU holds its own copy of the array from the library's load until the process
+ *    ends; its device address is looked up on the first call with that GPU current.
+ *  - Every call on one GPU shares that GPU's array and it keeps the last call's
+ *    contents: calls that may overlap on one GPU (different streams, or different host
+ *    threads) race and must be serialised by the caller.  No content needs clearing
+ *    between calls.
+ */
+int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const float* sinks,
+                             const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                             int64_t total_kv, int32_t max_kv_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                             int32_t causal, int32_t num_splits, void* out, float* lse,
+                             const sink_attn_rope* rope, void* stream);
+
+/* Bytes of the no-allocation entry point's scratch array on each GPU (its size limit). */
+size_t sink_attn_decode_noalloc_scratch_bytes(void);
 
 /* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
  * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot): S slots of

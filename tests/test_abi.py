@@ -159,7 +159,7 @@ def test_workspace_bytes(lib):
 
 
 def test_status_strings(lib):
-    for rc in range(6):
+    for rc in range(7):
         assert lib.sink_attn_status_str(rc).decode().startswith("SINK_ATTN_")
     assert b"unknown" in lib.sink_attn_status_str(99)
     assert re.match(rb"\d+\.\d+\.\d+", lib.sink_attn_version())
@@ -377,3 +377,21 @@ def test_kv_append_rejects_misaligned(lib):
                   a["vc"], None, None)
     for key in ("kn", "vn", "kc", "vc"):
         assert acall(**{key: odd}) == INVALID, key
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode validates like sink_attn_decode and rejects inputs whose
+    workspace would exceed its scratch array, all before any HIP call."""
+    f = lib.sink_attn_decode_noalloc
+    assert lib.sink_attn_decode_noalloc_scratch_bytes() == 32 << 20
+    def call(**kw):
+        a = dict(q=FAKE, ind=FAKE, batch=256, ql=4, tk=256 * 32768, maxk=32768, hq=64, hkv=4,
+                 d=128, ns=32, out=FAKE)
+        a.update(kw)
+        return f(a["q"], FAKE, FAKE, None, a["ind"], a["batch"], a["ql"], a["tk"], a["maxk"],
+                 a["hq"], a["hkv"], a["d"], 0.088, 1, a["ns"], a["out"], None, None, None)
+    assert call() == 6                                   # speculative-decode batch: too large
+    assert call(ns=0) == 6
+    assert call(q=None) == INVALID and call(out=None) == INVALID and call(ind=None) == INVALID
+    assert call(ql=5) == UNSUPPORTED and call(hq=63) == INVALID and call(ns=65) == INVALID
+    assert b"SCRATCH_LIMIT" in lib.sink_attn_status_str(6)

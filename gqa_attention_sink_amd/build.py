@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libsinkattn.so")
 HOST_SAN_LIB = os.path.join(PKG, "libsinkattn_host_asan.so")
+PEAK_LIB = os.path.join(PKG, "libsinkattn_peak.so")   # achievable-peak probes (bench only)
 HOST_SOURCES = ["api.cpp"]
 HIP_SOURCES = ["runtime.hip", "noalloc.hip", "prefill.hip", "decode.hip", "decode_stream.hip", "kv_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -61,6 +62,9 @@ def build(verbose: bool = False) -> str:
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    _run([HIPCC, *FLAGS, "-x", "hip", os.path.join(CSRC, "peak_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 

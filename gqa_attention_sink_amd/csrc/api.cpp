@@ -29,10 +29,39 @@ inline bool dim_ok(int d) { return d == 64 || d == 128; }
 
 inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-// Largest chunk count of the decode plan: the kernels apply the same rule
-// (sa::plan_chunks) to each sequence, and it is nondecreasing in the length.
-inline int planned_chunks(int32_t max_kv_len, int32_t num_splits, int cw) {
-  return sa::plan_chunks(max_kv_len, num_splits, cw);
+// Decode slot plan.  The kernels derive each sequence's chunk plan themselves
+// (sa::plan_chunks); the host fixes how chunks group into partial slots:
+//  - at most 16 rows per KV head: the chunk-wave kernel streams cw = 4 (head_dim 64) or
+//    2 (128) consecutive chunks in parallel, one per wavefront, and merges them;
+//  - otherwise the split kernel streams a run of consecutive chunks in turn.  With a
+//    forced chunk count the run is as long as keeps about four workgroups per compute
+//    unit (two rounds of the two that fit), so long runs stream unbroken and few
+//    partials are written; in planner mode the run is one chunk.
+// slots = ceil(n_max / chunks per slot), n_max the chunk count at max_kv_len (the plan
+// is nondecreasing in the length).
+constexpr int kRunWgsPerCu = 4;
+struct SlotPlan {
+  int cw;     // chunks per workgroup in parallel (chunk-wave kernel) or 1
+  int run;    // chunks per workgroup in turn (split kernel) or 1
+  int slots;  // partial slots per row
+};
+SlotPlan slot_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
+                   int32_t max_kv_len, int32_t num_splits, int cus) {
+  const int rows = q_len * (hq / hkv);
+  SlotPlan p{};
+  p.cw = sa::decode_chunk_waves(rows, d);
+  const int n = sa::plan_chunks(max_kv_len, num_splits, p.cw);
+  p.run = 1;
+  if (p.cw == 1 && num_splits > 0) {
+    const int w = sa::decode_waves(rows);
+    const int64_t row_groups = (rows + 16 * w - 1) / (16 * w);
+    const int64_t wgs = (int64_t)n * batch * hkv * row_groups;  // workgroups at runs of one
+    const int64_t r = wgs / ((int64_t)kRunWgsPerCu * cus);
+    p.run = (int)(r < 1 ? 1 : (r > n ? n : r));
+  }
+  const int per_slot = p.cw > 1 ? p.cw : p.run;
+  p.slots = (n + per_slot - 1) / per_slot;
+  return p;
 }
 
 // Compute units the planners size grids for: the caller's count if positive, else the
@@ -41,15 +70,6 @@ inline int resolve_cus(int32_t num_cus) {
   if (num_cus > 0) return num_cus;
   const int c = sa::device_cu_count();
   return c > 0 ? c : 256;
-}
-
-// Partial slots per row: one per group of cw consecutive chunks.
-inline int planned_slots(int32_t max_kv_len, int32_t num_splits, int cw) {
-  return (planned_chunks(max_kv_len, num_splits, cw) + cw - 1) / cw;
-}
-
-inline int chunk_waves(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
-  return sa::decode_chunk_waves(q_len * (hq / hkv), d);
 }
 
 // Stream decode plan (contiguous K/V, at most 64 query rows per KV head, planner mode,
@@ -62,8 +82,10 @@ constexpr int kStreamWavesPerCu = 4;
 constexpr int kStreamGroupsPerCu = 2;
 inline bool stream_eligible(int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
                             int32_t max_kv_len, int32_t num_splits) {
-  return num_splits == 0 && q_len * (hq / hkv) <= 64 &&
-         planned_slots(max_kv_len, num_splits, chunk_waves(q_len, hq, hkv, d)) > 1;
+  if (num_splits != 0 || q_len * (hq / hkv) > 64) return false;
+  // planner mode, whenever the chunk plan would need more than one slot (the batch and
+  // compute units do not matter in planner mode)
+  return slot_plan(1, q_len, hq, hkv, d, max_kv_len, 0, 256).slots > 1;
 }
 inline int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
 sa::StreamPlan stream_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv,
@@ -138,9 +160,9 @@ int check_decode_args(const void* q, const void* k, const void* v, const int32_t
 }
 
 sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const float* sinks,
-                           const int32_t* kv_indptr, int32_t q_len, int64_t total_kv,
-                           int32_t max_kv_len, int32_t hq, int32_t hkv, int32_t d,
-                           float sm_scale, int32_t causal, int32_t num_splits) {
+                           const int32_t* kv_indptr, int32_t batch, int32_t q_len,
+                           int64_t total_kv, int32_t max_kv_len, int32_t hq, int32_t hkv,
+                           int32_t d, float sm_scale, int32_t causal, int32_t num_splits) {
   sa::DecodeArgs a{};
   a.q = q;
   a.k = k;
@@ -156,8 +178,10 @@ sa::DecodeArgs decode_args(const void* q, const void* k, const void* v, const fl
   a.row_groups = (rows + 16 * w - 1) / (16 * w);
   a.num_splits = num_splits;
   a.num_kv_heads = hkv;
-  a.chunk_waves = chunk_waves(q_len, hq, hkv, d);
-  a.num_slots = planned_slots(max_kv_len, num_splits, a.chunk_waves);
+  const SlotPlan sp = slot_plan(batch, q_len, hq, hkv, d, max_kv_len, num_splits, resolve_cus(0));
+  a.chunk_waves = sp.cw;
+  a.chunk_run = sp.run;
+  a.num_slots = sp.slots;
   a.causal = causal;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return a;
@@ -421,10 +445,22 @@ static bool slot_args_ok(int32_t q_len, int32_t hq, int32_t hkv, int32_t d) {
   return q_len >= 1 && q_len <= 4 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && dim_ok(d);
 }
 
-int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
-                                         int32_t num_kv_heads, int32_t head_dim) {
-  if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim)) return 0;
-  return chunk_waves(q_len, num_q_heads, num_kv_heads, head_dim);
+static bool plan_args_ok(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv, int32_t d,
+                         int32_t max_kv_len, int32_t num_splits, int32_t num_cus) {
+  return batch >= 1 && slot_args_ok(q_len, hq, hkv, d) && max_kv_len >= 0 && num_splits >= 0 &&
+         num_splits <= kMaxSplits && num_cus >= 0;
+}
+
+int32_t sink_attn_decode_chunks_per_slot(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_kv_len, int32_t num_splits,
+                                         int32_t num_cus) {
+  if (!plan_args_ok(batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits,
+                    num_cus))
+    return 0;
+  const SlotPlan sp = slot_plan(batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                                num_splits, resolve_cus(num_cus));
+  return sp.cw > 1 ? sp.cw : sp.run;
 }
 
 int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num_q_heads,
@@ -433,8 +469,8 @@ int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num
   if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || kv_len < 0 ||
       num_splits < 0 || num_splits > kMaxSplits || capacity < 0 || (capacity > 0 && !bounds))
     return 0;
-  const int n = sa::plan_chunks(kv_len, num_splits, chunk_waves(q_len, num_q_heads, num_kv_heads,
-                                                                head_dim));
+  const int cw = sa::decode_chunk_waves(q_len * (num_q_heads / num_kv_heads), head_dim);
+  const int n = sa::plan_chunks(kv_len, num_splits, cw);
   const int cl = sa::chunk_len(kv_len, n);
   for (int c = 0; c <= n && c < capacity; ++c) {
     const int64_t a = (int64_t)c * cl;
@@ -443,21 +479,21 @@ int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num
   return n;
 }
 
-int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t max_kv_len, int32_t num_splits) {
-  if (!slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || max_kv_len < 0 ||
-      num_splits < 0 || num_splits > kMaxSplits)
+int32_t sink_attn_decode_num_slots(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                   int32_t num_splits, int32_t num_cus) {
+  if (!plan_args_ok(batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits,
+                    num_cus))
     return 0;
-  return planned_slots(max_kv_len, num_splits,
-                       chunk_waves(q_len, num_q_heads, num_kv_heads, head_dim));
+  return slot_plan(batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits,
+                   resolve_cus(num_cus)).slots;
 }
 
 size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_kv_len, int32_t num_splits) {
-  if (batch < 1) return 0;
-  const int64_t S = sink_attn_decode_num_slots(q_len, num_q_heads, num_kv_heads, head_dim,
-                                               max_kv_len, num_splits);
+  const int64_t S = sink_attn_decode_num_slots(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                               max_kv_len, num_splits, 0);
   if (S == 0) return 0;
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
   // the stream plan (contiguous caches) needs up to kStreamMaxSlots slots per row
@@ -481,7 +517,7 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
     if (rc != SINK_ATTN_OK) return rc;
     if (!part_o || !part_lse) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
     a.part_o = part_o;
@@ -531,7 +567,7 @@ static int stream_step(bool partial, const void* q, const void* k, const void* v
                                                        head_dim, max_kv_len, 0);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return SINK_ATTN_ERR_WORKSPACE;
-  sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+  sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                  num_q_heads, num_kv_heads, head_dim, sm_scale, causal, 0);
   sa::RopeArgs ra;
   if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
@@ -590,7 +626,7 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
     if (rc != SINK_ATTN_OK) return rc;
     if (!out) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
     sa::RopeArgs ra;
@@ -623,7 +659,7 @@ int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const 
     void* scratch = nullptr;
     const hipError_t e = sa::noalloc_scratch(&scratch);
     if (e != hipSuccess) return hip_fail(e);
-    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, q_len, total_kv, max_kv_len,
+    sa::DecodeArgs a = decode_args(q, k, v, sinks, kv_indptr, batch, q_len, total_kv, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
     return run_decode(a, batch, q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len,
@@ -654,7 +690,7 @@ int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
     if (rc != SINK_ATTN_OK) return rc;
     if (!out) return SINK_ATTN_ERR_INVALID_ARG;
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
-    sa::DecodeArgs a = decode_args(q, k_cache, v_cache, sinks, nullptr, q_len, 0, max_kv_len,
+    sa::DecodeArgs a = decode_args(q, k_cache, v_cache, sinks, nullptr, batch, q_len, 0, max_kv_len,
                                    num_q_heads, num_kv_heads, head_dim, sm_scale, causal,
                                    num_splits);
     a.kv_page_indptr = kv_page_indptr;

@@ -43,13 +43,20 @@ __device__ __forceinline__ void page_views(const DecodeArgs& a, const int32_t* _
 }
 
 // Decode split kernel.  Workgroup = W wavefronts = one (sequence, KV head, row group,
-// chunk); wavefront w owns 16 query rows.  The chunk's K and V stream from HBM into an
-// NST-stage LDS ring with asynchronous 16-byte buffer->LDS copies (no registers),
-// NST-1 stages ahead of the compute, and every wavefront reads each stage from LDS.
+// slot); wavefront w owns 16 query rows.  A slot holds a run of a.chunk_run consecutive
+// chunks of the plan: their keys are one contiguous span, which streams from HBM into an
+// NST-stage LDS ring with asynchronous 16-byte buffer->LDS copies (no registers), NST-1
+// stages ahead of the compute, every wavefront reading each stage from LDS.  Each chunk
+// keeps its own online softmax ("Sink attention": blocks of the key axis; the sink in
+// the first block only): chunk 0 starts from (sink, 1), every other chunk from
+// (-inf, 0), and at the end of each chunk its state is merged by log-sum-exp into the
+// run's state, which the slot writes.  A chunk is a whole number of 32-key stages, and
+// stages are counted from the run's first key, so the result for a sequence does not
+// depend on where it sits in the batch.
 template <int D, int W, bool DIRECT, bool PAGED>
-__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
-                                                              const int32_t* __restrict__ page_ids,
-                                                              RopeArgs rope) {
+__global__ __launch_bounds__(64 * W, 2) void decode_split_kernel(DecodeArgs a,
+                                                                 const int32_t* __restrict__ page_ids,
+                                                                 RopeArgs rope) {
   constexpr int KS = D / 32;              // k-steps (32 head dims) of S^T
   constexpr int DPL = D / 16;             // head dims per lane per V row read = O^T d-tiles
   constexpr int ROW = D * 2;              // bytes per K/V row
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int cg = lane >> 4;
-  const int c = blockIdx.x;
+  const int slot = blockIdx.x;
   const int g = blockIdx.y / a.row_groups;
   const int rg = blockIdx.y - g * a.row_groups;
   const int b = blockIdx.z;
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
   const int n = plan_chunks(lk, a.num_splits, 1);
   const int cl = chunk_len(lk, n);
   const int S = a.num_slots;
+  const int run = a.chunk_run;
 
   // The lane's query row: R -> (draft token t, query head h).
   const int R = rg * 16 * W + wave * 16 + l16;
@@ -95,21 +103,23 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
   const bool row_ok = R < M;
   const int64_t qrow = ((int64_t)b * a.q_len + row_t) * Hq + row_h;
 
-  if (c >= n) {  // unused slot: no mass
-    if (!DIRECT && cg == 0 && row_ok) a.part_lse[qrow * S + c] = kNegInf;
+  const int c_first = slot * run;  // first chunk of this slot's run
+  if (c_first >= n) {  // unused slot: no mass
+    if (!DIRECT && cg == 0 && row_ok) a.part_lse[qrow * S + slot] = kNegInf;
     return;
   }
-  const int kb = min(lk, c * cl);
-  const int ke = min(lk, kb + cl);
+  const int kb = (int)min<int64_t>(lk, (int64_t)c_first * cl);
+  const int ke = (int)min<int64_t>(lk, (int64_t)min(c_first + run, n) * cl);
   const int nsteps = (ke - kb + STEP - 1) / STEP;
+  const int chunk_steps = max(cl / STEP, 1);  // stages per chunk
 
-  // K/V of this chunk: loads past the chunk end return zero.  Contiguous HND: one view
-  // of the chunk.  Paged: a 32-key stage spans at most two pages (page_size is a
-  // multiple of 16), and each copy instruction's rows lie inside one of them.
+  // K/V of this run: loads past its end return zero.  Contiguous HND: one view of the
+  // run.  Paged: a 32-key stage spans at most two pages (page_size is a multiple of 16),
+  // and each copy instruction's rows lie inside one of them.
   const size_t head_base = PAGED ? 0 : ((size_t)g * a.total_kv + kv0 + kb) * D;
-  const uint32_t chunk_bytes = PAGED ? 0u : (uint32_t)(ke - kb) * ROW;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, chunk_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, chunk_bytes);
+  const uint32_t run_bytes = PAGED ? 0u : (uint32_t)(ke - kb) * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const __bf16*)a.k + head_base, run_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const __bf16*)a.v + head_base, run_bytes);
   auto issue = [&](int st) {
     unsigned char* kbuf = ring[st % NST][0];
     unsigned char* vbuf = ring[st % NST][1];
@@ -163,26 +173,41 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) rope_rotate8(qop[ks], qop[ks + KS / 2], ks * 32 + cg * 8, pos, rope);
   }
-  // Online-softmax state in log2 units; the sink joins chunk 0 only and is counted by
-  // one lane of the four that share a row.
+  // Online-softmax state of the current chunk in log2 units (the sink joins chunk 0
+  // only and is counted by one lane of the four that share a row), and the merged state
+  // of the run's finished chunks.
   float sig = kNegInf;
-  if (c == 0 && a.sinks != nullptr && row_ok) sig = a.sinks[row_h] * kLog2e;
+  if (c_first == 0 && a.sinks != nullptr && row_ok) sig = a.sinks[row_h] * kLog2e;
   float m = sig;
   float dsum = (sig != kNegInf && cg == 0) ? 1.0f : 0.0f;
   f32x4 o[DPL];
 #pragma unroll
   for (int t = 0; t < DPL; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float am = kNegInf, ad = 0.f;
+  f32x4 ao[DPL];
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) ao[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fold_chunk = [&]() {
+    const float mn = fmaxf(am, m);
+    const float ca = (am == kNegInf) ? 0.f : fast_exp2(am - mn);
+    const float cm = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
+    ad = __builtin_fmaf(dsum, cm, ad * ca);
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) ao[t] = o[t] * cm + ao[t] * ca;
+    am = mn;
+  };
 
   const float sl2 = a.scale_log2;
   const int causal_first_masked = a.causal ? (lk - a.q_len + 1) : 0x7fffffff;
   const int lim = min(ke - 1, a.causal ? lk - a.q_len + row_t : 0x7fffffff);
 
-  // Stages are issued unconditionally: a stage past the chunk end reads zeros through
+  // Stages are issued unconditionally: a stage past the run end reads zeros through
   // the bounded descriptor (no memory traffic), which keeps the copy count per stage
   // constant so one fixed wait suffices.
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) issue(st);
 
+  int in_chunk = 0;  // stages of the current chunk done
   for (int st = 0; st < nsteps; ++st) {
     // stage st has landed once only the NST-2 stages issued after it are pending
     wait_vmcnt<((NST - 2) * 2 * NDMA < 63 ? (NST - 2) * 2 * NDMA : 63)>();
@@ -206,7 +231,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
       }
       s2[kt] = acc;
     }
-    // ---- mask: keys past the chunk end, and (causal) keys after the row's position
+    // ---- mask: keys past the run end, and (causal) keys after the row's position
     if (kbase + STEP > ke || kbase + STEP > causal_first_masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -276,22 +301,32 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
       }
       o[t] = mfma16(as_bf16x8(va), pop, o[t]);
     }
+    // ---- chunk end: merge its state into the run's and start the next chunk
+    if (++in_chunk == chunk_steps && st + 1 < nsteps) {
+      fold_chunk();
+      in_chunk = 0;
+      m = kNegInf;
+      dsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
+  fold_chunk();
 
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
   // ---- epilogue: lane holds head dims [4*cg*DPL, +4*DPL) of its row; O^T element
   // (t, j) is head dim DPL*(4*cg + j) + t.
-  float dr = wave_xor_sum(dsum, 16);
+  float dr = wave_xor_sum(ad, 16);
   dr = wave_xor_sum(dr, 32);
   if (!row_ok) return;
   const float inv = dr > 0.f ? 1.0f / dr : 0.f;
-  const float lse_nat = dr > 0.f ? (m + __builtin_log2f(dr)) * kLn2 : kNegInf;
+  const float lse_nat = dr > 0.f ? (am + __builtin_log2f(dr)) * kLn2 : kNegInf;
   float vals[4 * DPL];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) vals[j * DPL + t] = o[t][j] * inv;
+    for (int t = 0; t < DPL; ++t) vals[j * DPL + t] = ao[t][j] * inv;
   const int d0 = 4 * cg * DPL;
   if constexpr (DIRECT) {
     uint32_t* dst = (uint32_t*)((__bf16*)a.out + qrow * D + d0);
@@ -306,11 +341,11 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a,
     }
     if (cg == 0 && a.lse != nullptr) a.lse[qrow] = lse_nat;
   } else {
-    float* dst = a.part_o + (qrow * S + c) * D + d0;
+    float* dst = a.part_o + (qrow * S + slot) * D + d0;
 #pragma unroll
     for (int e = 0; e < 4 * DPL; e += 4)
       *(f32x4*)(dst + e) = f32x4{vals[e], vals[e + 1], vals[e + 2], vals[e + 3]};
-    if (cg == 0) a.part_lse[qrow * S + c] = lse_nat;
+    if (cg == 0) a.part_lse[qrow * S + slot] = lse_nat;
   }
 }
 

@@ -1,0 +1,94 @@
+// Achievable-peak probes for the measurement harness (not part of the attention path):
+// how fast this chip streams HBM with the read pattern the decode kernels use, and how
+// many bf16 MFMA flops it sustains when nothing else runs.  The attention kernels'
+// roofline fractions are quoted against the spec-sheet peaks; these give the measured
+// ceilings beside them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sink_attn_peak.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // 16-byte loads in flight per lane
+
+// Every 16-byte piece of [p, p + n16*16) is read once, with the non-temporal policy the
+// decode kernels use.  Like them, each workgroup streams one contiguous span (its share
+// of the buffer, in order); lane i of a wavefront reads piece i of a contiguous KiB, so
+// every load instruction is one coalesced KiB, and kUnroll loads per lane are in flight.
+// Indices stay inside [begin, end) by construction.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ p,
+                                                               int64_t n16, uint32_t* out) {
+  const int64_t span = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t begin = (int64_t)blockIdx.x * span;
+  const int64_t end = begin + span < n16 ? begin + span : n16;
+  int64_t i = begin + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kUnroll - 1) * kThreads < end; i += kUnroll * kThreads) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) v[k] = __builtin_nontemporal_load(p + i + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < end; i += kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // the loads must not be removed: the result is stored in the rare case it matches
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+// Eight independent chains of v_mfma_f32_32x32x16_bf16 per wavefront, no memory traffic
+// inside the loop; each lane stores one sum at the end (out has grid * 256 floats).
+__global__ __launch_bounds__(kThreads) void mfma_loop_kernel(int iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(0.001f * (float)((lane + j) & 7));
+    b[j] = (__bf16)(0.002f * (float)((lane * 3 + j) & 7));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][15];
+  out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sink_attn_peak_stream_read(const void* buf, size_t bytes, int32_t num_blocks, void* out4,
+                               void* stream) {
+  if (!buf || !out4 || bytes == 0 || (bytes & 15u) != 0 || ((uintptr_t)buf & 15u) != 0 ||
+      num_blocks < 1)
+    return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)num_blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const u32x4*)buf, (int64_t)(bytes / 16),
+                     (uint32_t*)out4);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int sink_attn_peak_mfma_bf16(int32_t iters, int32_t num_blocks, float* out, void* stream) {
+  if (!out || iters < 1 || num_blocks < 1) return 1;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3((unsigned)num_blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (int)iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

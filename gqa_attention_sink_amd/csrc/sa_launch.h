@@ -62,7 +62,8 @@ struct DecodeArgs {
   int32_t row_groups;  // ceil(q_len * group / (16 * decode_waves(q_len * group)))
   int32_t num_splits;  // 0 = planner
   int32_t num_slots;   // partial slots per row (chunk groups of chunk_waves chunks)
-  int32_t chunk_waves; // chunks one workgroup takes together (1: split kernel; 4 or 2: chunk-wave kernel)
+  int32_t chunk_waves; // chunks one workgroup takes in parallel (4 or 2: chunk-wave kernel; 1: split kernel)
+  int32_t chunk_run;   // split kernel: consecutive chunks one workgroup takes in turn (a slot)
   int32_t causal;
   float scale_log2;
   float* part_o;       // [rows, num_slots, D]   (split mode)

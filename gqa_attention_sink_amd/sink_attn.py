@@ -60,8 +60,8 @@ _SIGS = {  # entry points that take a rope pointer have it just before the strea
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "sink_attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
-    "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32] * 6),
-    "sink_attn_decode_chunks_per_slot": (ctypes.c_int32, [ctypes.c_int32] * 4),
+    "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32] * 8),
+    "sink_attn_decode_chunks_per_slot": (ctypes.c_int32, [ctypes.c_int32] * 8),
     "sink_attn_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -259,9 +259,13 @@ def prefill_workspace_bytes(total_q: int, num_q_heads: int, head_dim: int, split
                                                         int(splits)))
 
 
-def decode_chunks_per_slot(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+def decode_chunks_per_slot(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_kv_len: int, num_splits: int = 0,
+                           num_cus: int = 0) -> int:
     """Consecutive plan chunks whose merged state one partial slot holds."""
-    return int(load().sink_attn_decode_chunks_per_slot(q_len, num_q_heads, num_kv_heads, head_dim))
+    return int(load().sink_attn_decode_chunks_per_slot(batch, q_len, num_q_heads, num_kv_heads,
+                                                       head_dim, int(max_kv_len),
+                                                       int(num_splits), int(num_cus)))
 
 
 def decode_chunk_bounds(kv_len: int, q_len: int, num_q_heads: int, num_kv_heads: int,
@@ -279,10 +283,12 @@ def decode_chunk_bounds(kv_len: int, q_len: int, num_q_heads: int, num_kv_heads:
     return list(buf)
 
 
-def decode_num_slots(q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                     max_kv_len: int, num_splits: int = 0) -> int:
-    return int(load().sink_attn_decode_num_slots(q_len, num_q_heads, num_kv_heads, head_dim,
-                                                 int(max_kv_len), int(num_splits)))
+def decode_num_slots(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, max_kv_len: int, num_splits: int = 0,
+                     num_cus: int = 0) -> int:
+    return int(load().sink_attn_decode_num_slots(batch, q_len, num_q_heads, num_kv_heads,
+                                                 head_dim, int(max_kv_len), int(num_splits),
+                                                 int(num_cus)))
 
 
 def decode_workspace_bytes(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
@@ -376,13 +382,14 @@ def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optiona
                    causal: bool = True, num_splits: int = 0, part_o=None, part_lse=None,
                    rope: Optional[RopeParams] = None):
     """First stage of decode alone.  Returns (part_o [B*q_len*Hq, S, D] fp32,
-    part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(q_len, Hq, Hkv, D, max_kv_len,
-    num_splits); slot j holds plan chunks [j*C, j*C + C), C = decode_chunks_per_slot(...)."""
+    part_lse [B*q_len*Hq, S] fp32) with S = decode_num_slots(B, q_len, Hq, Hkv, D,
+    max_kv_len, num_splits); slot j holds plan chunks [j*C, j*C + C), C =
+    decode_chunks_per_slot(...)."""
     lib = load()
     b, ql, hq, d, hkv, tk = _decode_common(q, k, v, kv_indptr)
     sinks = _sinks_arg(sinks, hq, q.device)
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-    s = decode_num_slots(ql, hq, hkv, d, max_kv_len, num_splits)
+    s = decode_num_slots(b, ql, hq, hkv, d, max_kv_len, num_splits)
     rows = b * ql * hq
     if part_o is None:
         part_o = torch.empty((rows, s, d), dtype=torch.float32, device=q.device)

@@ -154,7 +154,11 @@ size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, i
  *             to [4, 16] chunks for each sequence, where C =
  *             sink_attn_decode_chunks_per_slot(...) is the number of chunks one
  *             workgroup takes together; k in 1..64 = exactly k chunks per sequence.  A
- *             chunk holds ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty.
+ *             chunk holds ceil(ceil(Lk/n)/32)*32 keys; trailing chunks may be empty
+ *             (sink_attn_decode_chunk_bounds).  Every chunk keeps its own online softmax,
+ *             chunk 0 starting from (sink, 1) and every other chunk from (-inf, 0), and the
+ *             chunks are merged by log-sum-exp: first the C chunks one workgroup takes
+ *             (in parallel, or in turn as one run of consecutive chunks), then the slots.
  *             With num_splits = 0, q_len * num_q_heads/num_kv_heads <= 64, total_kv <
  *             2^31 and more than one partial slot (see sink_attn_decode_num_slots), the
  *             stream plan is used instead: each KV head's token axis (all sequences back
@@ -213,12 +217,21 @@ size_t sink_attn_decode_workspace_bytes(int32_t batch, int32_t q_len, int32_t nu
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_kv_len, int32_t num_splits);
 
-/* Chunks per partial slot, C: with q_len * (num_q_heads/num_kv_heads) <= 16 rows per KV
- * head one workgroup streams C consecutive chunks in parallel (one wavefront each, C = 4
- * for head_dim 64 and 2 for 128) and merges them before writing; otherwise C = 1.
- * 0 if the arguments are invalid. */
-int32_t sink_attn_decode_chunks_per_slot(int32_t q_len, int32_t num_q_heads,
-                                         int32_t num_kv_heads, int32_t head_dim);
+/* Chunks per partial slot, C (0 if the arguments are invalid).  With
+ * q_len * (num_q_heads/num_kv_heads) <= 16 rows per KV head one workgroup streams C
+ * consecutive chunks in parallel (one wavefront each, C = 4 for head_dim 64 and 2 for
+ * 128) and merges them before writing.  Otherwise one workgroup streams a run of C
+ * consecutive chunks in turn, each chunk with its own online softmax, merging each
+ * finished chunk into the run's state: C = 1 in planner mode, and with a forced chunk
+ * count k the longest run that still gives about four workgroups per compute unit,
+ * C = clamp(floor(k * batch * num_kv_heads * row_groups / (4 * num_cus)), 1, k), with
+ * row_groups = ceil(rows / 64) (1 for rows <= 64).  num_cus: compute units to plan for,
+ * 0 = the current device's (what sink_attn_decode uses), or 256 when no device is
+ * current. */
+int32_t sink_attn_decode_chunks_per_slot(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_kv_len, int32_t num_splits,
+                                         int32_t num_cus);
 
 /* Chunk plan of one sequence with kv_len keys ("Sink attention": blocks along the key
  * axis; the pages fix no size): the number of chunks n (0 if the arguments are invalid)
@@ -229,19 +242,22 @@ int32_t sink_attn_decode_chunk_bounds(int32_t kv_len, int32_t q_len, int32_t num
                                       int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
                                       int32_t* bounds, int32_t capacity);
 
-/* Partial slots per row the decode path uses (the S of the partial layout):
- * ceil(n_max / C) with n_max the planner's chunk count at max_kv_len.  0 if invalid. */
-int32_t sink_attn_decode_num_slots(int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t max_kv_len, int32_t num_splits);
+/* Partial slots per row the chunk kernels use (the S of the partial layout):
+ * ceil(n_max / C) with n_max the chunk count at max_kv_len and C as above; num_cus as
+ * above.  0 if the arguments are invalid. */
+int32_t sink_attn_decode_num_slots(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                   int32_t num_splits, int32_t num_cus);
 
 /*
  * First stage of sink_attn_decode on its own: for every row
  * r = (b*q_len + t)*num_q_heads + h and slot j < S, the normalised output
  * part_o[r][j][0..head_dim) (fp32) and natural-log partition function part_lse[r][j]
  * (fp32; -inf when empty) of the keys of plan chunks [j*C, j*C + C) together (chunk 0
- * includes the sink).  S = sink_attn_decode_num_slots(...), C =
- * sink_attn_decode_chunks_per_slot(...).  Exported so the partials can be checked and
- * timed; sink_attn_decode = this + merge (with S = 1 the kernel writes the result).
+ * includes the sink).  S = sink_attn_decode_num_slots(..., 0), C =
+ * sink_attn_decode_chunks_per_slot(..., 0) (planned for the current device).  Exported
+ * so the partials can be checked and timed; sink_attn_decode = this + merge (with S = 1
+ * the kernel writes the result).
  */
 int sink_attn_decode_partial(const void* q, const void* k, const void* v,
                              const float* sinks, const int32_t* kv_indptr, int32_t batch,

@@ -115,17 +115,31 @@ def test_merge_validation(lib):
 
 
 def test_planner_slots(lib):
-    ns = lib.sink_attn_decode_num_slots
-    cps = lib.sink_attn_decode_chunks_per_slot
-    # one wavefront per chunk when q_len*G > 16 (here 4 x 8 = 32 rows): slots = chunks
+    def ns(ql, hq, hkv, d, maxk, splits, batch=1, cus=256):
+        return lib.sink_attn_decode_num_slots(batch, ql, hq, hkv, d, maxk, splits, cus)
+    def cps(ql, hq, hkv, d, maxk=1024, splits=0, batch=1, cus=256):
+        return lib.sink_attn_decode_chunks_per_slot(batch, ql, hq, hkv, d, maxk, splits, cus)
+    # planner mode, more than 16 rows per KV head (here 4 x 8 = 32): one chunk per slot
     assert cps(4, 32, 4, 64) == 1
     assert ns(4, 32, 4, 64, 8192, 0) == 16 and ns(4, 32, 4, 64, 1024, 0) == 4
     assert ns(4, 32, 4, 64, 100, 0) == 4 and ns(4, 32, 4, 64, 0, 0) == 4
     assert ns(4, 32, 4, 64, 2049, 0) == 9 and ns(4, 32, 4, 64, 100000, 0) == 16
-    assert ns(4, 32, 4, 64, 32768, 32) == 32 and ns(4, 32, 4, 64, 10, 1) == 1
+    assert ns(4, 32, 4, 64, 10, 1) == 1
+    # forced chunks, more than 16 rows: runs of chunks, as long as about four workgroups
+    # per CU remain.  Speculative decode (256 x 4 KV heads, 32 chunks): 32768 chunk
+    # workgroups / 1024 -> runs of 32, one slot; a single sequence: runs of 1
+    assert cps(4, 64, 4, 128, 32768, 32, batch=256) == 32
+    assert ns(4, 64, 4, 128, 32768, 32, batch=256) == 1
+    assert cps(4, 64, 4, 128, 32768, 32, batch=1) == 1 and ns(4, 64, 4, 128, 32768, 32) == 32
+    assert cps(4, 64, 4, 128, 32768, 32, batch=64) == 8          # 8192 / 1024
+    assert ns(4, 64, 4, 128, 32768, 32, batch=64) == 4
+    assert cps(4, 64, 4, 128, 32768, 32, batch=64, cus=80) == 25  # 8192 / 320
+    assert ns(4, 64, 4, 128, 32768, 32, batch=64, cus=80) == 2
+    assert cps(4, 64, 2, 128, 32768, 7, batch=300) == 7           # rows 128: 2 row groups
     # <= 16 rows: 4 chunks per slot (head_dim 64) or 2 (head_dim 128); the planner rounds
     # ceil(Lk/256) up to a multiple of that before clamping to [4, 16]
     assert cps(1, 64, 8, 64) == 4 and cps(1, 64, 8, 128) == 2 and cps(2, 16, 2, 64) == 4
+    assert cps(1, 64, 8, 64, 32768, 32, batch=500) == 4          # forced: same grouping
     assert ns(1, 64, 8, 64, 8192, 0) == 4 and ns(1, 64, 8, 64, 1024, 0) == 1
     assert ns(1, 64, 8, 64, 1025, 0) == 2 and ns(1, 64, 8, 64, 3000, 0) == 3
     assert ns(1, 64, 8, 128, 2049, 0) == 5 and ns(1, 64, 8, 128, 100, 0) == 2
@@ -134,11 +148,14 @@ def test_planner_slots(lib):
     assert ns(1, 64, 8, 64, 10, 65) == 0 and ns(1, 64, 8, 64, -1, 0) == 0
     assert ns(0, 64, 8, 64, 10, 0) == 0 and ns(1, 64, 7, 64, 10, 0) == 0
     assert ns(1, 64, 8, 96, 10, 0) == 0 and cps(5, 64, 8, 64) == 0
+    assert ns(1, 64, 8, 64, 10, 0, batch=0) == 0 and ns(1, 64, 8, 64, 10, 0, cus=-1) == 0
 
 
 def test_workspace_bytes(lib):
     wb = lib.sink_attn_decode_workspace_bytes
-    rows, s, d = 256 * 4 * 64, 32, 128
+    # speculative decode, 32 chunks: runs of 32 chunks per workgroup on 256 CUs (the
+    # planned-for count with no device), so one slot
+    rows, s, d = 256 * 4 * 64, 1, 128
     o = rows * s * d * 4
     o = (o + 255) // 256 * 256
     expect = (o + rows * s * 4 + 255) // 256 * 256
@@ -303,7 +320,7 @@ def test_decode_chunk_plan_is_a_partition(lib, ql, hq, hkv, d):
     """The plan the kernels derive per sequence: a partition of [0, Lk) into equal
     32-key-aligned chunks (trailing ones may be empty); the planner picks 4..16 chunks,
     a multiple of the chunks one workgroup merges; a forced count is taken as given."""
-    cps = lib.sink_attn_decode_chunks_per_slot(ql, hq, hkv, d)
+    cps = lib.sink_attn_decode_chunks_per_slot(1, ql, hq, hkv, d, 1024, 0, 256)
     for lk in (0, 1, 31, 32, 33, 255, 256, 1000, 1024, 1025, 4097, 8192, 32768, 100000):
         for ns in (0, 1, 3, 7, 32, 64):
             b = _bounds(lib, lk, ql, hq, hkv, d, ns)

@@ -294,7 +294,7 @@ def test_decode_partials_match_oracle_chunks(sa, ns):
                                True, ns)
     torch.cuda.synchronize()
     s = pl.shape[1]
-    cps = sa.decode_chunks_per_slot(2, 16, 4, 64)
+    cps = sa.decode_chunks_per_slot(len(lens), 2, 16, 4, 64, w.max_kv, ns)
     assert cps == 4  # 8 rows per KV head: four chunks per slot
     bounds = []
     for lk in lens:
@@ -477,3 +477,104 @@ def test_determinism(sa):
     torch.cuda.synchronize()
     assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
     assert torch.equal(b1[0], b2[0]) and torch.equal(b1[1], b2[1])
+
+
+# ------------------------------------------------------------------ runs of chunks
+# Forced chunk counts with more than 16 query rows per KV head: a workgroup streams a
+# run of C consecutive chunks in turn, each chunk its own online softmax (chunk 0 from
+# the sink), merged by log-sum-exp into the run's partial; C grows with the batch so
+# about four workgroups per CU remain (C and the slots come from the library).
+RUN_CASES = [
+    # batch, length range, q_len, hq, hkv, d, sink, causal, num_splits
+    (40, (0, 700), 4, 32, 4, 64, ("normal", 0, 2), True, 64),         # 32 rows, runs ~10
+    (64, (200, 2000), 4, 64, 4, 128, ("alt_neginf", 2, 1), True, 16),  # 64 rows, runs ~4
+    (256, (33, 400), 4, 64, 4, 128, ("normal", 0, 2), True, 32),      # one slot: direct
+    (24, (1, 3000), 3, 96, 4, 64, ("normal", 4, 1), False, 40),       # 72 rows: 2 row groups
+]
+
+
+def _run_case(case, device="cuda"):
+    bsz, (lo, hi), ql, hq, hkv, d, sink, causal, ns = RUN_CASES[case]
+    rng = np.random.default_rng(880 + case)
+    lens = [int(x) for x in rng.integers(lo, hi + 1, size=bsz)]
+    lens[0] = 0 if lo == 0 else lens[0]            # an empty sequence where allowed
+    return wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, ns,
+                          seed=860 + case, device=device), lens
+
+
+@pytest.mark.parametrize("case", range(len(RUN_CASES)))
+def test_decode_runs_partials_match_oracle(sa, case):
+    """Slot j of a row = plan chunks [j*C, j*C + C) of its sequence, each an independent
+    softmax (chunk 0 with the sink), merged: the oracle's chunk form over the library's
+    chunk bounds, its chunk partials merged in the same groups."""
+    w, lens = _run_case(case)
+    bsz, ql, hq, hkv, d, ns = w.batch, w.q_len, w.hq, w.hkv, w.d, w.num_splits
+    s = sa.decode_num_slots(bsz, ql, hq, hkv, d, w.max_kv, ns)
+    cps = sa.decode_chunks_per_slot(bsz, ql, hq, hkv, d, w.max_kv, ns)
+    _say(f"run partials case {case}: B={bsz} ns={ns} chunks/slot={cps} slots={s}")
+    assert s == -(-ns // cps)
+    if s == 1:
+        pytest.skip("one slot: the kernel writes the result (checked by the decode test)")
+    po, pl = sa.decode_partial(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                               w.causal, ns)
+    torch.cuda.synchronize()
+    bounds = [sa.decode_chunk_bounds(lk, ql, hq, hkv, d, ns) for lk in lens]
+    cu_q = torch.arange(bsz + 1, dtype=torch.int32) * ql
+    _, _, rpo, rpl = oracle.sink_attention_chunked(w.q.reshape(-1, hq, d), w.k, w.v, w.sinks,
+                                                   cu_q, w.cu_seqlens_kv.cpu(), w.scale,
+                                                   w.causal, bounds, return_partials=True)
+    rpo = rpo.reshape(-1, ns, d)
+    rpl = rpl.reshape(-1, ns)
+    go, gl = _np(po), _np(pl)
+    for j in range(s):
+        ro, rl = oracle.merge_partials(rpo[:, j * cps:(j + 1) * cps], rpl[:, j * cps:(j + 1) * cps])
+        assert np.array_equal(np.isneginf(gl[:, j]), np.isneginf(rl)), f"slot {j}: -inf pattern"
+        fin = np.isfinite(rl)
+        if fin.any():
+            assert np.abs(gl[fin, j] - rl[fin]).max() <= LSE_TOL, f"slot {j}: lse"
+            err = np.abs(go[fin, j] - ro[fin])
+            assert err.max() <= 1e-2 and err.mean() <= 1e-3, f"slot {j}: partial output"
+
+
+@pytest.mark.parametrize("case", range(len(RUN_CASES)))
+def test_decode_runs_match_oracle(sa, case):
+    w, lens = _run_case(case)
+    _say(f"run decode case {case}: B={w.batch} ns={w.num_splits}")
+    out, lse = _run_decode(sa, w)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_decode(w)
+    _compare(out, lse, ro, rl, f"run decode case {case}")
+    for b, lk in enumerate(lens):   # no keys: zero output and lse = the sink (chunk 0 empty),
+        if lk == 0:                 # up to the rounding of the log2-domain state
+            assert float(out[b].abs().max()) == 0.0
+            sk = w.sinks.float().cpu().expand(w.q_len, w.hq)
+            assert torch.allclose(lse[b].cpu(), sk, rtol=1e-6, atol=1e-6)
+
+
+def test_decode_runs_offsets_and_neighbours_bitwise(sa):
+    """Same batch size (so the same plan), sequences in reverse order, at other offsets,
+    behind and before NaN tokens: every sequence's output and lse are bitwise those of
+    the packed batch (stages, chunks and runs are counted from each sequence's first
+    key)."""
+    w, lens = _run_case(0)
+    ns = w.num_splits
+    assert sa.decode_chunks_per_slot(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, ns) > 1
+    _say("run decode: reordered and gapped batch, bitwise")
+    o1, l1 = _run_decode(sa, w)
+    order = list(range(w.batch))[::-1]
+    gap = 37
+    ind = w.cu_seqlens_kv.cpu().tolist()
+    hkv, _, d = w.k.shape
+    nan = torch.full((hkv, gap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    # sequences back to back (the kv_indptr convention) in reverse order, with NaN
+    # tokens before the first and after the last
+    k3 = torch.cat([nan] + [w.k[:, ind[b]:ind[b + 1]] for b in order] + [nan], dim=1).contiguous()
+    v3 = torch.cat([nan] + [w.v[:, ind[b]:ind[b + 1]] for b in order] + [nan], dim=1).contiguous()
+    ind3 = torch.tensor(np.concatenate([[0], np.cumsum([lens[b] for b in order])]) + gap,
+                        dtype=torch.int32, device="cuda")
+    q3 = w.q[order].contiguous()
+    o3, l3 = sa.decode(q3, k3, v3, w.sinks, ind3, w.max_kv, w.scale, w.causal, ns)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o3.float()).all()
+    for i, b in enumerate(order):
+        assert torch.equal(o3[i], o1[b]) and torch.equal(l3[i], l1[b]), f"sequence {b}"

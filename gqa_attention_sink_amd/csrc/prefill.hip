@@ -362,12 +362,6 @@ __device__ __forceinline__ void matrix_sched() {
     matrix_sched<I + 1, N, NQ, LA>();
   }
 }
-template <int NQ, int LA>
-constexpr int first_reads() {
-  int c = 0;
-  for (int i = 0; i < LA; ++i) c += operand_reads<NQ, LA>(i);
-  return c;
-}
 
 // Workgroup barrier that also fences the instruction scheduler, so that no
 // instruction of one phase is moved into the neighbouring phase.
@@ -541,6 +535,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
   constexpr int NQ = 2 * C::KS;
   constexpr int NP = 4 * C::DT;
   constexpr int LA = 6;
+  // K operands 0 .. LA-1 of the next matrix phase, read during the vector phase before it
+  u32x4 kpre[LA];
+  auto preload_k = [&](int jk) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)((u0 + jk) & 3) * C::UB;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      kpre[i] = *(const u32x4*)(sm.k[0] + (kb + koff[i >> 1] + (i & 1) * 32 * C::ROW));
+  };
   auto matrix_ops = [&](int jk, int jv, int jc, auto qk_tag, auto pv_tag) __attribute__((always_inline)) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
     u32x2 vlo[NP], vhi[NP];
     auto reads = [&](int i) __attribute__((always_inline)) {
       if (i < NQ) {
-        if (QK) kop[i] = *(const u32x4*)(sm.k[0] + (kb + koff[i >> 1] + (i & 1) * 32 * C::ROW));
+        if (QK) kop[i] = i < LA ? kpre[i] : *(const u32x4*)(sm.k[0] + (kb + koff[i >> 1] + (i & 1) * 32 * C::ROW));
       } else if (PV) {
         const int q = (i - NQ) / C::DT, t = (i - NQ) % C::DT;
         const int ro = ((q >> 1) * 32 + 16 * (q & 1)) * C::ROW;
@@ -585,7 +587,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
         else copy_block(u0 + jc + 2, true, c - C::NDMA);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first_reads<NQ, LA>(), 0);
     matrix_sched<0, NQ + NP, NQ, LA>();
   };
   // One code path for every step (the MFMA accumulators then keep their registers):
@@ -674,16 +675,24 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a, RopeA
   // loop; group 0 balances it after the loop), so both groups execute the same loop body.
   // The matrix phase of step j also copies this wavefront's half of K(j+3) and V(j+2)
   // into the slots of K(j-1) and V(j-2), whose last readers finished before h = 2j.
-  // Before the barrier that starts h = 2j each wavefront waits for its copies of K(j) and
-  // V(j-1), which precede those of the two later steps.
+  // Each vector phase first reads the leading K operands of the wavefront's next matrix
+  // phase, so that phase's MFMAs start without waiting on the LDS.  Hence K(j) and V(j-1)
+  // must be complete before the barrier that starts h = 2j, and K(j+1) before the one
+  // that starts h = 2j+1; the waits before each barrier leave in flight only the copy
+  // groups (one tensor of one unit each) issued after those: group 0 issues at h = 2c,
+  // so 5 after a matrix phase and 4 after a vector phase, group 1 at h = 2c+1, so 4 and 3.
   phase_barrier();
   if (grp == 1) phase_barrier();
+  preload_k(0);
   for (int j = 0; j <= n; ++j) {
     matrix_phase(j);
-    if (grp == 1) wait_vmcnt<2 * 2 * C::NDMA>();
+    if (grp == 0) wait_vmcnt<5 * C::NDMA>();
+    else wait_vmcnt<4 * C::NDMA>();
     phase_barrier();
+    preload_k(j + 1);
     vector_phase(j);
-    if (grp == 0) wait_vmcnt<2 * 2 * C::NDMA>();
+    if (grp == 0) wait_vmcnt<4 * C::NDMA>();
+    else wait_vmcnt<3 * C::NDMA>();
     phase_barrier();
   }
   if (grp == 0) phase_barrier();

@@ -668,9 +668,11 @@ __global__ __launch_bounds__(64 * W) void decode_stream_wg_kernel(
 
 // Merge of the stream partials: row (b, t, h) combines the partials of the ranges that
 // overlap sequence b with the sink of head h, a term of value zero and log-sum-exp
-// sink[h].  D/4 lanes per row, four consecutive head dims each.  All of a row's loads
-// (at most kStreamMaxSlots slots, read once: non-temporal) are issued together, so a row
-// waits for one memory latency, not one per slot.
+// sink[h].  D/4 lanes per row, four consecutive head dims each.  The sequence bounds and
+// the row's log-sum-exps (4 bytes a slot) are loaded together; then only the partial
+// outputs of the n slots this call wrote (read once: non-temporal) are loaded, all
+// together, so a row waits for two memory latencies and reads n, not kStreamMaxSlots,
+// partial outputs.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamPlan sp,
                                                            int64_t rows) {
@@ -685,15 +687,10 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
   const int S = sp.smax;
   const float* pl = a.part_lse + row * S;
   const f32x4* po = (const f32x4*)(a.part_o + row * S * D) + q;
-  // every slot of the row is read (the workspace holds S per row) together with the
-  // sequence bounds; slots past the sequence's last range are masked afterwards
   float lc[kStreamMaxSlots];
   f32x4 x[kStreamMaxSlots];
 #pragma unroll
   for (int c = 0; c < kStreamMaxSlots; ++c) lc[c] = (c < S) ? __builtin_nontemporal_load(pl + c) : kNegInf;
-#pragma unroll
-  for (int c = 0; c < kStreamMaxSlots; ++c)
-    x[c] = (c < S) ? __builtin_nontemporal_load(po + (size_t)c * (D / 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
   const float sink = (a.sinks != nullptr) ? a.sinks[h] : kNegInf;
   int s0, e0;
   if constexpr (PAGED) {  // the sequence's extent on the page-list axis
@@ -706,12 +703,11 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a, StreamP
   }
   const int n = (e0 > s0) ? min(S, (e0 - 1) / sp.R - s0 / sp.R + 1) : 0;
 #pragma unroll
-  for (int c = 0; c < kStreamMaxSlots; ++c) {
-    if (c >= n) {  // not written by this call: no weight, output selected away
-      lc[c] = kNegInf;
-      x[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  for (int c = 0; c < kStreamMaxSlots; ++c)
+    x[c] = (c < n) ? __builtin_nontemporal_load(po + (size_t)c * (D / 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kStreamMaxSlots; ++c)
+    if (c >= n) lc[c] = kNegInf;  // not written by this call: no weight
   float mx = sink;
 #pragma unroll
   for (int c = 0; c < kStreamMaxSlots; ++c) mx = fmaxf(mx, lc[c]);

@@ -492,7 +492,9 @@ def tiny_line(sa, steps, warmup, flush, cpu_budget):
 def peaks(w, steps, warmup, flush):
     """Achievable rates measured on this GPU: a flat non-temporal read of the headline's
     K and V (the same bytes, one launch each, every workgroup streaming one contiguous
-    share), and a register-only bf16 MFMA loop with two wavefronts per SIMD."""
+    share), a register-only bf16 MFMA loop with two wavefronts per SIMD, and the MFMA rate
+    of one chain per SIMD beside 0-4 exp2+FMA pairs per MFMA (the softmax's vector work)
+    issued by the same wavefront or by the other wavefront of the SIMD."""
     from gqa_attention_sink_amd import build as bld
     lib = ctypes.CDLL(bld.PEAK_LIB)
     lib.sink_attn_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
@@ -514,6 +516,18 @@ def peaks(w, steps, warmup, flush):
     sm, _ = time_calls([mf], steps, warmup, flush)
     flops = blocks * 4 * iters * 8 * 32768
     tf = flops / (sm["median"] * 1e-3) / 1e12
+    # one MFMA chain per SIMD with E exp2+FMA pairs per MFMA, issued by the same
+    # wavefront or by a second wavefront on the SIMD
+    lib.sink_attn_peak_coissue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    cb, ci = cus, 1024
+    outc = torch.empty(cb * 512, dtype=torch.float32, device="cuda")
+    co = {"same_wavefront": {}, "other_wavefront": {}}
+    for split, key in ((0, "same_wavefront"), (1, "other_wavefront")):
+        for e in range(5):
+            fn = _c_call(lib.sink_attn_peak_coissue, (e, split, ci, cb, ctypes.c_void_p(outc.data_ptr()), st))
+            sc, _ = time_calls([fn], steps, warmup, flush)
+            co[key][str(e)] = round(cb * 4 * ci * 8 * 32768 / (sc["median"] * 1e-3) / 1e12, 1)
     return {"hbm_flat_read": {"GB/s": round(hbm, 1), "frac_of_spec": round(hbm / HBM_PEAK_GBS, 4),
                               "bytes": 2 * kb, "ms": _r(s["median"]),
                               "what": f"non-temporal 16-byte loads over {w.name}'s K and V, "
@@ -522,6 +536,10 @@ def peaks(w, steps, warmup, flush):
                                "ms": _r(sm["median"]),
                                "what": f"{blocks} workgroups x 4 wavefronts, 8 independent "
                                        "32x32x16 MFMA chains each, no memory traffic"},
+            "mfma_beside_exp_TFLOP/s": dict(co, what=f"{cb} workgroups, one 32x32x16 MFMA chain "
+                                                     "per SIMD; key = exp2+FMA pairs per MFMA, "
+                                                     "issued after each MFMA by the same "
+                                                     "wavefront or by the SIMD's second one"),
             "compute_units": cus}
 
 

@@ -1,6 +1,7 @@
 // Achievable-peak probes for the measurement harness (not part of the attention path):
-// how fast this chip streams HBM with the read pattern the decode kernels use, and how
-// many bf16 MFMA flops it sustains when nothing else runs.  The attention kernels'
+// how fast this chip streams HBM with the read pattern the decode kernels use, how many
+// bf16 MFMA flops it sustains when nothing else runs, and how many when softmax-like
+// vector work shares the SIMD (issued by the same wavefront or by its neighbour).  The attention kernels'
 // roofline fractions are quoted against the spec-sheet peaks; these give the measured
 // ceilings beside them.
 #include <hip/hip_runtime.h>
@@ -69,6 +70,68 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(int iters, float* o
   out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// MFMA issue beside softmax-like vector work: per v_mfma_f32_32x32x16_bf16 of a chain,
+// E pairs of one FMA and one exp2 (the arithmetic of one score of an online softmax), on
+// independent registers.
+//   SPLIT false: workgroups of 4 wavefronts (one per SIMD); each issues MFMA i and then
+//     its E pairs, in that order (fenced from the scheduler), as a wavefront that
+//     software-pipelines its own exponentials against its own MFMAs would.
+//   SPLIT true: workgroups of 8 wavefronts (two per SIMD); wavefronts 0-3 issue only the
+//     MFMAs, 4-7 only the pairs, E per MFMA of the neighbour, as in a ping-pong schedule.
+// Either way the MFMA chains are those of mfma_loop_kernel's first four wavefronts.
+template <int E, bool SPLIT>
+__global__ __launch_bounds__(512) void coissue_kernel(int iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  float s = 0.f;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.01f * (float)((lane + j) & 15);
+  if (!SPLIT || w < 4) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = (__bf16)(0.001f * (float)((lane + j) & 7));
+      b[j] = (__bf16)(0.002f * (float)((lane * 3 + j) & 7));
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        if (!SPLIT) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            x[(c * E + e) & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[(c * E + e) & 7], 0.999f, -0.001f));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][15];
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int e = 0; e < 8 * E; ++e) x[e & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e & 7], 0.999f, -0.001f));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[(int64_t)blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+template <int E>
+void launch_coissue(bool split, int iters, int blocks, float* out, hipStream_t st) {
+  if (split)
+    hipLaunchKernelGGL((coissue_kernel<E, true>), dim3((unsigned)blocks), dim3(512), 0, st, iters, out);
+  else
+    hipLaunchKernelGGL((coissue_kernel<E, false>), dim3((unsigned)blocks), dim3(256), 0, st, iters, out);
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +151,20 @@ int sink_attn_peak_mfma_bf16(int32_t iters, int32_t num_blocks, float* out, void
   if (!out || iters < 1 || num_blocks < 1) return 1;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3((unsigned)num_blocks), dim3(kThreads), 0,
                      (hipStream_t)stream, (int)iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int sink_attn_peak_coissue(int32_t pairs_per_mfma, int32_t split, int32_t iters,
+                           int32_t num_blocks, float* out, void* stream) {
+  if (!out || iters < 1 || num_blocks < 1 || pairs_per_mfma < 0 || pairs_per_mfma > 4) return 1;
+  const hipStream_t st = (hipStream_t)stream;
+  switch (pairs_per_mfma) {
+    case 0: launch_coissue<0>(split != 0, iters, num_blocks, out, st); break;
+    case 1: launch_coissue<1>(split != 0, iters, num_blocks, out, st); break;
+    case 2: launch_coissue<2>(split != 0, iters, num_blocks, out, st); break;
+    case 3: launch_coissue<3>(split != 0, iters, num_blocks, out, st); break;
+    default: launch_coissue<4>(split != 0, iters, num_blocks, out, st); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -28,6 +28,15 @@ int sink_attn_peak_stream_read(const void* buf, size_t bytes, int32_t num_blocks
  * 32768 flops.  out: num_blocks * 256 floats of device memory. */
 int sink_attn_peak_mfma_bf16(int32_t iters, int32_t num_blocks, float* out, void* stream);
 
+/* MFMA chains beside vector work: num_blocks workgroups, 4 wavefronts of each issuing
+ * iters x 8 v_mfma_f32_32x32x16_bf16 as sink_attn_peak_mfma_bf16 does (num_blocks * 4 *
+ * iters * 8 * 32768 flops), with pairs_per_mfma (0-4) pairs of one FMA and one exp2 per
+ * MFMA: split = 0: issued by the MFMA wavefront itself after each MFMA (4 wavefronts a
+ * workgroup, one per SIMD); split != 0: by a second wavefront on the same SIMD (8
+ * wavefronts a workgroup).  out: num_blocks * 512 floats of device memory. */
+int sink_attn_peak_coissue(int32_t pairs_per_mfma, int32_t split, int32_t iters,
+                           int32_t num_blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

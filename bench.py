@@ -394,13 +394,18 @@ def prefill_line(sa, w, steps, warmup, flush, cpu_budget, num_splits=1):
     fl = prefill_flops(w)
     tf = fl / (whole["median"] * 1e-3) / 1e12
     kname = "prefill_kernel" if w.d == 64 else "prefill_pp_kernel"
+    # HBM bytes if every tensor moved once: Q, K, V read, O and lse written
+    min_bytes = 2 * tq * w.hq * w.d * 2 + 2 * tk * w.hkv * w.d * 2 + tq * w.hq * 4
+    traffic = _traffic_for(kname, w.name) if ns == 1 else None
     line = {"TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "ms": _r(whole["median"]), "ms_min": _r(whole["min"]), "ms_mean": _r(whole["mean"]),
-            "steps": whole["n"], "flops": fl, "key_splits": ns,
+            "steps": whole["n"], "flops": fl, "key_splits": ns, "min_hbm_bytes": min_bytes,
             "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                          "note": "whole call (one kernel" + (", plus the merge)" if ns > 1 else ")")}}
+    if traffic:
+        line["traffic_over_min_hbm_bytes"] = round(traffic / min_bytes, 3)
     if cpu_budget:
         line["cpu_baseline"] = cpu_prefill(w, cpu_budget)
     return line

@@ -334,7 +334,7 @@ def decode_line(sa, w, steps, warmup, flush, cpu_budget):
                            (P(w.q), P(w.k), P(w.v), P(w.sinks), P(w.cu_seqlens_kv), w.batch,
                             w.q_len, tk, mk, w.hq, w.hkv, w.d, scale, causal, ns, P(po), P(pl),
                             None, st))
-            merge = _c_call(lib.sink_attn_merge, (P(po), P(pl), rows, slots, w.d, P(out), P(lse), st))
+            merge = _c_call(lib.sink_attn_merge, (P(po), P(pl), None, rows, slots, w.d, P(out), P(lse), st))
             steps_alone = [part, merge]
     t0 = time.perf_counter()
     whole, _ = time_calls([full], steps, warmup, flush)

@@ -263,7 +263,7 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
   a.part_lse = (float*)((char*)workspace + obytes);
   hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, false, page_ids, rope, st);
   if (e != hipSuccess) return hip_fail(e);
-  e = sa::launch_merge(a.part_o, a.part_lse, rows, a.num_slots, head_dim, out, lse, st);
+  e = sa::launch_merge(a.part_o, a.part_lse, nullptr, rows, a.num_slots, head_dim, out, lse, st);
   if (e != hipSuccess) return hip_fail(e);
   return SINK_ATTN_OK;
 }
@@ -379,7 +379,7 @@ static int prefill_common(const void* q, const void* k, const void* v, const flo
   a.part_lse = (float*)((char*)workspace + obytes);
   hipError_t e = sa::launch_prefill(a, head_dim, num_kv_heads, ra, st);
   if (e != hipSuccess) return hip_fail(e);
-  e = sa::launch_merge(a.part_o, a.part_lse, rows, S, head_dim, out, lse, st);
+  e = sa::launch_merge(a.part_o, a.part_lse, nullptr, rows, S, head_dim, out, lse, st);
   if (e != hipSuccess) return hip_fail(e);
   return SINK_ATTN_OK;
 }
@@ -777,16 +777,17 @@ int sink_attn_rope_apply(void* x, int64_t num_tokens, int32_t num_heads, int32_t
   }
 }
 
-int sink_attn_merge(const float* part_o, const float* part_lse, int64_t rows, int32_t num_slots,
-                    int32_t head_dim, void* out, float* lse, void* stream) {
+int sink_attn_merge(const float* part_o, const float* part_lse, const int32_t* splits_per_row,
+                    int64_t rows, int32_t num_slots, int32_t head_dim, void* out, float* lse,
+                    void* stream) {
   try {
     if (!part_o || !part_lse || !out || rows < 0) return SINK_ATTN_ERR_INVALID_ARG;
     if (num_slots < 1 || num_slots > kMaxSlots) return SINK_ATTN_ERR_INVALID_ARG;
     if (!dim_ok(head_dim)) return SINK_ATTN_ERR_UNSUPPORTED;
     if ((rows + 3) / 4 > 0x7fffffffLL) return SINK_ATTN_ERR_UNSUPPORTED;
     if (rows == 0) return SINK_ATTN_OK;
-    hipError_t e = sa::launch_merge(part_o, part_lse, rows, num_slots, head_dim, out, lse,
-                                    (hipStream_t)stream);
+    hipError_t e = sa::launch_merge(part_o, part_lse, splits_per_row, rows, num_slots, head_dim,
+                                    out, lse, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   } catch (...) {

@@ -674,11 +674,13 @@ __global__ __launch_bounds__(64 * CW) void decode_cw_kernel(DecodeArgs a,
 // Slots are taken eight at a time, their loads issued together (eight in flight per
 // lane measured 11 % faster than four on 32 slots).  A slot with lse = -inf has weight 0
 // and its partial output (possibly never written) is selected away, never multiplied.
-// The partials are read once, with the non-temporal cache policy.
+// The partials are read once, with the non-temporal cache policy.  counts (optional): row r
+// merges only its first counts[r] slots (clamped to [0, S]); the rest are not read.
 constexpr int kMergeThreads = 128;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
                                                               const float* __restrict__ part_lse,
+                                                              const int32_t* __restrict__ counts,
                                                               int64_t rows, int S, __bf16* out,
                                                               float* lse) {
   constexpr int LPR = D / 4;
@@ -688,24 +690,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   if (row >= rows) return;
   const float* pl = part_lse + row * S;
   const f32x4* po = (const f32x4*)(part_o + row * S * D) + q;
+  const int n = counts != nullptr ? min(max(counts[row], 0), S) : S;
   float mx = kNegInf;
-  for (int c = 0; c < S; c += 8) {
+  for (int c = 0; c < n; c += 8) {
     float t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = (c + u < S) ? __builtin_nontemporal_load(pl + c + u) : kNegInf;
+    for (int u = 0; u < 8; ++u) t[u] = (c + u < n) ? __builtin_nontemporal_load(pl + c + u) : kNegInf;
 #pragma unroll
     for (int u = 0; u < 8; ++u) mx = fmaxf(mx, t[u]);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int c = 0; c < S; c += 8) {
+  if (mx != kNegInf) {  // then n >= 1
+    for (int c = 0; c < n; c += 8) {
       float w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = (c + u < S) ? __expf(__builtin_nontemporal_load(pl + c + u) - mx) : 0.f;
+      for (int u = 0; u < 8; ++u) w[u] = (c + u < n) ? __expf(__builtin_nontemporal_load(pl + c + u) - mx) : 0.f;
       f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(po + (size_t)min(c + u, S - 1) * (D / 4));
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(po + (size_t)min(c + u, n - 1) * (D / 4));
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         wsum += w[u];
@@ -763,14 +766,15 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int batch, int
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows, int num_slots,
-                        int head_dim, void* out, float* lse, hipStream_t stream) {
+hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* counts,
+                        int64_t rows, int num_slots, int head_dim, void* out, float* lse,
+                        hipStream_t stream) {
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)((rows + 7) / 8)), dim3(kMergeThreads),
-                       0, stream, part_o, part_lse, rows, num_slots, (__bf16*)out, lse);
+                       0, stream, part_o, part_lse, counts, rows, num_slots, (__bf16*)out, lse);
   else
     hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)((rows + 3) / 4)), dim3(kMergeThreads),
-                       0, stream, part_o, part_lse, rows, num_slots, (__bf16*)out, lse);
+                       0, stream, part_o, part_lse, counts, rows, num_slots, (__bf16*)out, lse);
   return hipGetLastError();
 }
 

@@ -36,8 +36,8 @@ hipError_t launch_merge_stream(const DecodeArgs&, int, const StreamPlan&, int64_
                                hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_merge(const float*, const float*, int64_t, int, int, void*, float*,
-                        hipStream_t) {
+hipError_t launch_merge(const float*, const float*, const int32_t*, int64_t, int, int, void*,
+                        float*, hipStream_t) {
   return hipErrorNoDevice;
 }
 

@@ -153,8 +153,9 @@ hipError_t launch_decode_stream(const DecodeArgs& a, int head_dim, const StreamP
                                 const RopeArgs& rope, const int32_t* page_ids, hipStream_t stream);
 hipError_t launch_merge_stream(const DecodeArgs& a, int head_dim, const StreamPlan& sp,
                                int64_t rows, bool paged, hipStream_t stream);
-hipError_t launch_merge(const float* part_o, const float* part_lse, int64_t rows,
-                        int num_slots, int head_dim, void* out, float* lse,
+// counts: valid slots per row (nullptr = all num_slots)
+hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* counts,
+                        int64_t rows, int num_slots, int head_dim, void* out, float* lse,
                         hipStream_t stream);
 
 }  // namespace sa

@@ -63,8 +63,8 @@ _SIGS = {  # entry points that take a rope pointer have it just before the strea
     "sink_attn_decode_num_slots": (ctypes.c_int32, [ctypes.c_int32] * 8),
     "sink_attn_decode_chunks_per_slot": (ctypes.c_int32, [ctypes.c_int32] * 8),
     "sink_attn_merge": (ctypes.c_int, [
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "sink_attn_decode_paged": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,      # q k v sinks
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                       # page table
@@ -470,20 +470,24 @@ def decode_stream_merge(sinks, kv_indptr, q_shape, total_kv: int, num_kv_heads: 
     return out, lse
 
 
-def merge(part_o, part_lse, out=None, lse=None, return_lse: bool = True):
+def merge(part_o, part_lse, out=None, lse=None, return_lse: bool = True, splits_per_row=None):
     """Log-sum-exp merge of partials: part_o [rows, S, D] fp32, part_lse [rows, S] fp32
-    -> (out [rows, D] bf16, lse [rows] fp32)."""
+    -> (out [rows, D] bf16, lse [rows] fp32).  splits_per_row: optional int32 [rows], the
+    number of leading slots each row merges (None = all S)."""
     lib = load()
     _dev_tensor(part_o, torch.float32, "part_o", 3)
     _dev_tensor(part_lse, torch.float32, "part_lse", 2)
     rows, s, d = part_o.shape
     _need(tuple(part_lse.shape) == (rows, s), "part_lse must be [rows, S]")
+    if splits_per_row is not None:
+        _dev_tensor(splits_per_row, torch.int32, "splits_per_row", 1)
+        _need(splits_per_row.numel() == rows, "splits_per_row must be [rows]")
     if out is None:
         out = torch.empty((rows, d), dtype=torch.bfloat16, device=part_o.device)
     if lse is None and return_lse:
         lse = torch.empty((rows,), dtype=torch.float32, device=part_o.device)
-    rc = lib.sink_attn_merge(_ptr(part_o), _ptr(part_lse), rows, s, d, _ptr(out), _ptr(lse),
-                             _stream(part_o.device))
+    rc = lib.sink_attn_merge(_ptr(part_o), _ptr(part_lse), _ptr(splits_per_row), rows, s, d,
+                             _ptr(out), _ptr(lse), _stream(part_o.device))
     _check(rc)
     return out, lse
 

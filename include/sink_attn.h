@@ -318,11 +318,14 @@ int sink_attn_decode_stream_merge(const float* sinks, const int32_t* kv_indptr, 
  * Slots with part_lse = -inf carry no weight (their part_o is not read); a row with
  * every slot -inf gets out = 0 and lse = -inf.
  *  part_o fp32 [rows, num_slots, head_dim], part_lse fp32 [rows, num_slots],
- *  num_slots 1..256, head_dim 64 or 128, out bf16 [rows, head_dim], lse fp32 [rows] or
- *  NULL.
+ *  splits_per_row int32 [rows] or NULL: row r merges only its first splits_per_row[r]
+ *  slots (clamped to [0, num_slots]; 0 gives out = 0, lse = -inf), whose lse and part_o
+ *  alone are read; NULL = every row merges all num_slots,
+ *  num_slots 1..256 (the row stride of part_o and part_lse), head_dim 64 or 128,
+ *  out bf16 [rows, head_dim], lse fp32 [rows] or NULL.
  */
-int sink_attn_merge(const float* part_o, const float* part_lse, int64_t rows,
-                    int32_t num_slots, int32_t head_dim, void* out, float* lse,
+int sink_attn_merge(const float* part_o, const float* part_lse, const int32_t* splits_per_row,
+                    int64_t rows, int32_t num_slots, int32_t head_dim, void* out, float* lse,
                     void* stream);
 
 /*

@@ -106,12 +106,13 @@ def test_decode_partial_validation(lib):
 
 def test_merge_validation(lib):
     m = lib.sink_attn_merge
-    assert m(None, FAKE, 4, 2, 64, FAKE, None, None) == INVALID
-    assert m(FAKE, FAKE, 4, 0, 64, FAKE, None, None) == INVALID
-    assert m(FAKE, FAKE, 4, 257, 64, FAKE, None, None) == INVALID
-    assert m(FAKE, FAKE, -1, 2, 64, FAKE, None, None) == INVALID
-    assert m(FAKE, FAKE, 4, 2, 72, FAKE, None, None) == UNSUPPORTED
-    assert m(FAKE, FAKE, 0, 2, 64, FAKE, None, None) == OK
+    assert m(None, FAKE, None, 4, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, None, 4, 0, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, FAKE, 4, 257, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, None, -1, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, None, 4, 2, 72, FAKE, None, None) == UNSUPPORTED
+    assert m(FAKE, FAKE, None, 0, 2, 64, FAKE, None, None) == OK
+    assert m(FAKE, FAKE, FAKE, 0, 2, 64, FAKE, None, None) == OK
 
 
 def test_planner_slots(lib):

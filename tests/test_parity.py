@@ -334,6 +334,33 @@ def test_merge_against_oracle(sa):
     assert torch.all(out[5] == 0) and torch.isneginf(lse[5])
 
 
+def test_merge_splits_per_row_against_oracle(sa):
+    """Per-row slot counts: row r merges only its first n_r slots (clamped to [0, S]).  The
+    slots past each row's count hold NaN, so a read of any of them would show."""
+    g = torch.Generator().manual_seed(11)
+    rows, s, d = 257, 12, 64
+    po = torch.randn(rows, s, d, generator=g)
+    pl = torch.randn(rows, s, generator=g) * 3
+    pl[torch.rand(rows, s, generator=g) < 0.2] = float("-inf")
+    n = torch.randint(0, s + 1, (rows,), generator=g, dtype=torch.int32)
+    n[:4] = torch.tensor([0, s, -3, s + 5], dtype=torch.int32)   # empty, full, clamped both ways
+    k = n.clamp(0, s)
+    for r in range(rows):
+        po[r, k[r]:] = float("nan")
+        pl[r, k[r]:] = float("nan")
+    _say("merge with splits_per_row")
+    out, lse = sa.merge(po.cuda(), pl.cuda(), splits_per_row=n.cuda())
+    torch.cuda.synchronize()
+    ro = np.zeros((rows, d))
+    rl = np.full(rows, -np.inf)
+    for r in range(rows):
+        if k[r] > 0:
+            o1, l1 = oracle.merge_partials(po[r:r + 1, :k[r]], pl[r:r + 1, :k[r]])
+            ro[r], rl[r] = np.asarray(o1)[0], np.asarray(l1)[0]
+    _compare(out, lse, ro, rl, "merge splits_per_row")
+    assert torch.all(out[0] == 0) and torch.isneginf(lse[0])
+
+
 def test_decode_split_invariance(sa):
     w = wl.make_decode([700, 3000, 64], 4, 16, 2, 128, ("normal", 0, 2), 1 / math.sqrt(128),
                        True, 0, seed=400, device="cuda")

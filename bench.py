@@ -235,9 +235,10 @@ def cpu_prefill(w, budget_s, rows=128):
                      f"{n} blocks of <= {rows} query rows of {w.name} (all heads)")
 
 
-def cpu_paged(w, pk, page_size, budget_s):
+def cpu_paged(w, pk, page_size, budget_s, rope=None):
     """The paged-cache oracle on whole sequences: their pages copied into a small host
-    cache with their own page table; GB/s of the sample's algorithmic bytes."""
+    cache with their own page table (with `rope`, the oracle's YaRN rotation of the
+    queries at positions Lk - q_len + t first); GB/s of the sample's algorithmic bytes."""
     import oracle
     ind = pk.kv_page_indptr.cpu().tolist()
     idx = pk.kv_page_indices.cpu().tolist()
@@ -248,22 +249,27 @@ def cpu_paged(w, pk, page_size, budget_s):
         kc = pk.k_cache[pages].cpu()
         vc = pk.v_cache[pages].cpu()
         q = w.q[b:b + 1].cpu()
+        lk = (len(pages) - 1) * page_size + last[b] if pages else 0
         t0 = time.perf_counter()
+        if rope is not None:
+            pos = (lk - w.q_len + np.arange(w.q_len))[None, :, None]
+            q = oracle.bf16_round(oracle.apply_rope(q, pos, **rope))
         oracle.sink_attention_decode_paged(q, kc, vc, w.sinks, [0, len(pages)],
                                            list(range(len(pages))), [last[b]], page_size,
                                            w.scale, w.causal)
         t_used += time.perf_counter() - t0
-        lk = (len(pages) - 1) * page_size + last[b] if pages else 0
-        done += lk * w.hkv * w.d * 4 + 2 * q.numel() * 2 + w.q_len * w.hq * 4 + len(pages) * 4
+        done += lk * w.hkv * w.d * 4 + 2 * w.q_len * w.hq * w.d * 2 + w.q_len * w.hq * 4 + len(pages) * 4
         n += 1
         if t_used >= budget_s:
             break
     return _baseline(done / t_used / 1e9, "GB/s", t_used,
-                     f"{n} of {w.batch} sequences of {w.name} in {page_size}-token pages")
+                     f"{n} of {w.batch} sequences of {w.name} in {page_size}-token pages" +
+                     (", queries rotated" if rope is not None else ""))
 
 
-def cpu_append(p, pk, k_new, v_new, page_size, budget_s):
-    """The append oracle on whole sequences (their pages in a small host cache); GB/s of
+def cpu_append(p, pk, k_new, v_new, page_size, budget_s, rope=None):
+    """The append oracle on whole sequences (their pages in a small host cache; with
+    `rope`, the oracle's YaRN rotation of the new keys at their positions first); GB/s of
     the new K/V read and written."""
     import oracle
     ind = pk.kv_page_indptr.cpu().tolist()
@@ -278,15 +284,20 @@ def cpu_append(p, pk, k_new, v_new, page_size, budget_s):
         kn = k_new[app[b]:app[b + 1]].cpu()
         vn = v_new[app[b]:app[b + 1]].cpu()
         t0 = time.perf_counter()
+        if rope is not None:
+            lk = (len(pages) - 1) * page_size + last[b] if pages else 0
+            pos = lk - kn.shape[0] + np.arange(kn.shape[0])
+            kn = oracle.bf16_round(oracle.apply_rope(kn, pos[:, None], **rope))
         oracle.kv_append(kc, vc, kn, vn, [0, kn.shape[0]], [0, len(pages)],
                          list(range(len(pages))), [last[b]], page_size)
         t_used += time.perf_counter() - t0
-        done += 2 * 2 * kn.numel() * 2
+        done += 2 * 2 * vn.numel() * 2
         n += 1
         if t_used >= budget_s:
             break
     return _baseline(done / t_used / 1e9, "GB/s", t_used,
-                     f"{n} of {p.batch} sequences of the varlen K/V appended")
+                     f"{n} of {p.batch} sequences of the varlen K/V appended" +
+                     (", keys rotated" if rope is not None else ""))
 
 
 # ---------------------------------------------------------------- GPU lines
@@ -449,6 +460,7 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
             res[name]["rope"] = YARN_BENCH
     if cpu_budget:
         res["paged_decode"]["cpu_baseline"] = cpu_paged(w, pk, 16, cpu_budget)
+        res["paged_decode_rope"]["cpu_baseline"] = cpu_paged(w, pk, 16, cpu_budget, YARN_BENCH)
     del pk, ws
     torch.cuda.empty_cache()
     p = wl.make("varlen_prefill", device="cuda")
@@ -473,6 +485,8 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
                                   "frac": round(g / HBM_PEAK_GBS, 4), "traffic": None}}
     if cpu_budget:
         res["kv_append"]["cpu_baseline"] = cpu_append(p, pk, k_new, v_new, 16, cpu_budget)
+        res["kv_append_rope"]["cpu_baseline"] = cpu_append(p, pk, k_new, v_new, 16, cpu_budget,
+                                                           YARN_BENCH)
     return res
 
 
@@ -660,7 +674,7 @@ def main():
         _say("spec_decode_planner")
         d5 = wl.make("spec_decode", device="cuda")
         d5.num_splits = 0
-        others["spec_decode_planner"] = decode_line(sa, d5, S, W, flush, 0)
+        others["spec_decode_planner"] = decode_line(sa, d5, S, W, flush, cpu_line)
         del d5
         torch.cuda.empty_cache()
         other_decode = "decode_gptoss" if args.workload == "spec_decode" else "spec_decode"

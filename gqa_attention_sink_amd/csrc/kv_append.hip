@@ -18,7 +18,7 @@
 namespace sa {
 
 constexpr int kAppendThreads = 256;
-constexpr int kAppendTok = 16;  // new tokens per workgroup
+constexpr int kAppendTok = 4;  // new tokens per workgroup
 
 template <int D>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a,

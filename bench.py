@@ -315,7 +315,8 @@ def decode_line(sa, w, steps, warmup, flush, cpu_budget):
     tk = w.k.shape[1]
     scale, causal, mk = float(w.scale), int(bool(w.causal)), int(w.max_kv)
     rows_per_head = w.q_len * (w.hq // w.hkv)
-    plan = sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, mk) if ns == 0 else None
+    kind = sa.decode_plan_kind(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, mk, ns)
+    plan = sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, mk) if kind == "stream" else None
     full = _c_call(lib.sink_attn_decode,
                    (P(w.q), P(w.k), P(w.v), P(w.sinks), P(w.cu_seqlens_kv), w.batch, w.q_len, tk,
                     mk, w.hq, w.hkv, w.d, scale, causal, ns, P(ws), ws.numel(), P(out), P(lse),
@@ -332,6 +333,10 @@ def decode_line(sa, w, steps, warmup, flush, cpu_budget):
         steps_alone = [part, merge]
         plan_desc = dict(kind="stream", range_tokens=plan[0], ranges_per_head=plan[1],
                          slots=plan[2])
+    elif kind == "whole_runs":  # one slot: the split kernel writes the result
+        slots = 1
+        kname = "decode_split_kernel"
+        plan_desc = dict(kind="whole_runs", chunks_per_slot="all", slots=1)
     else:
         slots = sa.decode_num_slots(w.batch, w.q_len, w.hq, w.hkv, w.d, mk, ns)
         cps = sa.decode_chunks_per_slot(w.batch, w.q_len, w.hq, w.hkv, w.d, mk, ns)
@@ -367,7 +372,9 @@ def decode_line(sa, w, steps, warmup, flush, cpu_budget):
             "num_splits": ns,
             "plan": (f"{ns} chunks per sequence, each its own online softmax (sink in chunk "
                      "0), merged by log-sum-exp") if ns else
-                    "planner: ranges of each KV head's token axis, sink added in the merge",
+                    ("planner: every chunk of a sequence in one workgroup (equal lengths, "
+                     "at least two workgroups per CU), merged inside it" if kind == "whole_runs"
+                     else "planner: ranges of each KV head's token axis, sink added in the merge"),
             "slot_plan": plan_desc,
             "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(kgbs, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),

@@ -14,6 +14,7 @@ from .sink_attn import (  # noqa: F401
     decode_noalloc_scratch_bytes,
     decode_num_slots,
     decode_paged,
+    decode_plan_kind,
     decode_partial,
     decode_stream_merge,
     decode_stream_partial,

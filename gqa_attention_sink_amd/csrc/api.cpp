@@ -106,6 +106,22 @@ sa::StreamPlan stream_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv
   p.num_kv_heads = hkv;
   return p;
 }
+// Whole-sequence runs (planner mode, contiguous K/V, more than 16 rows per KV head): when
+// the batch alone gives at least kWholeRunWgsPerCu workgroups per compute unit and the
+// sequences are of nearly equal length (total_kv >= 7/8 of batch * max_kv_len), one
+// workgroup per (sequence, KV head, row group) streams every chunk of its sequence in
+// turn and writes the result: the work is already balanced, so the stream plan's equal
+// ranges, its partials and its merge buy nothing.
+constexpr int kWholeRunWgsPerCu = 2;
+inline bool whole_runs(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv, int64_t total_kv,
+                       int32_t max_kv_len, int32_t num_splits, int cus) {
+  const int rows = q_len * (hq / hkv);
+  if (num_splits != 0 || rows <= 16 || max_kv_len < 1) return false;
+  const int w = sa::decode_waves(rows);
+  const int64_t row_groups = (rows + 16 * w - 1) / (16 * w);
+  const int64_t wgs = (int64_t)batch * hkv * row_groups;
+  return wgs >= (int64_t)kWholeRunWgsPerCu * cus && 8 * total_kv >= 7 * (int64_t)batch * max_kv_len;
+}
 inline size_t partial_bytes(int64_t rows, int64_t slots, int d) {
   int64_t bytes = rows * slots * d * 4;   // partial outputs
   bytes = (bytes + 255) & ~(int64_t)255;
@@ -224,6 +240,18 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
   hipStream_t st = (hipStream_t)stream;
   // A paged cache streams along its page list laid end to end (single-wavefront plans).
   const bool paged = page_ids != nullptr;
+  if (!paged && whole_runs(batch, q_len, num_q_heads, num_kv_heads, a.total_kv, max_kv_len,
+                           num_splits, resolve_cus(0))) {
+    // one slot holding every chunk of the plan at max_kv_len (a sequence's own plan has
+    // no more chunks): the split kernel writes the result
+    a.chunk_run = sa::plan_chunks(max_kv_len, 0, 1);
+    a.num_slots = 1;
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, nullptr, rope, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SINK_ATTN_OK;
+  }
   const int64_t axis = paged ? a.num_page_entries * (int64_t)a.page_size : a.total_kv;
   if (axis <= INT32_MAX && (!paged || q_len * (num_q_heads / num_kv_heads) <= 16) &&
       stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits)) {
@@ -531,6 +559,21 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v, const 
   } catch (...) {
     return SINK_ATTN_ERR_INTERNAL;
   }
+}
+
+int32_t sink_attn_decode_plan_kind(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
+                                   int32_t max_kv_len, int32_t num_splits, int32_t num_cus) {
+  if (batch < 1 || !slot_args_ok(q_len, num_q_heads, num_kv_heads, head_dim) || total_kv < 0 ||
+      max_kv_len < 0 || num_splits < 0 || num_splits > kMaxSplits || num_cus < 0)
+    return -1;
+  const int cus = resolve_cus(num_cus);
+  if (whole_runs(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len, num_splits, cus))
+    return SINK_ATTN_PLAN_WHOLE_RUNS;
+  if (total_kv <= INT32_MAX &&
+      stream_eligible(q_len, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits))
+    return SINK_ATTN_PLAN_STREAM;
+  return SINK_ATTN_PLAN_CHUNKS;
 }
 
 int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,

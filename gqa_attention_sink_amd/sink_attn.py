@@ -100,6 +100,9 @@ _SIGS["sink_attn_decode_stream_plan"] = (ctypes.c_int32, [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)])
+_SIGS["sink_attn_decode_plan_kind"] = (ctypes.c_int32, [
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32])
 _SIGS["sink_attn_decode_chunk_bounds"] = (ctypes.c_int32, [
     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
     ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32])
@@ -407,10 +410,28 @@ def decode_partial(q, k, v, sinks, kv_indptr, max_kv_len: int, sm_scale: Optiona
     return part_o, part_lse
 
 
+DECODE_PLANS = {0: "chunks", 1: "stream", 2: "whole_runs"}
+
+
+def decode_plan_kind(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, total_kv: int, max_kv_len: int, num_splits: int = 0,
+                     num_cus: int = 0) -> str:
+    """Which plan decode() uses for these sizes (contiguous K/V): "chunks", "stream" or
+    "whole_runs".  num_cus = 0 plans for the current device."""
+    k = load().sink_attn_decode_plan_kind(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                          int(total_kv), int(max_kv_len), int(num_splits),
+                                          int(num_cus))
+    if k < 0:
+        raise ValueError("invalid decode sizes")
+    return DECODE_PLANS[k]
+
+
 def decode_stream_plan(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
                        head_dim: int, total_kv: int, max_kv_len: int, num_cus: int = 0):
-    """(R, ranges_per_head, slots) of the stream plan decode() uses for these sizes, or
-    None when it uses the chunk plan.  num_cus = 0 plans for the current device."""
+    """(R, ranges_per_head, slots) of the stream plan for these sizes (what the stream
+    step entry points use, and decode() too unless decode_plan_kind() says
+    "whole_runs"), or None when it does not apply.  num_cus = 0 plans for the current
+    device."""
     r, n, s = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     ok = load().sink_attn_decode_stream_plan(batch, q_len, num_q_heads, num_kv_heads, head_dim,
                                              int(total_kv), int(max_kv_len), int(num_cus),

@@ -165,7 +165,14 @@ size_t sink_attn_prefill_workspace_bytes(int64_t total_q, int32_t num_q_heads, i
  *             to back) is cut into equal ranges of R tokens, each streamed by one
  *             wavefront (<= 16 rows) or by one workgroup of 2 or 4 wavefronts that
  *             share the staged keys (<= 32 / <= 64 rows), whose partials are merged
- *             with the sinks (sink_attn_decode_stream_plan).
+ *             with the sinks (sink_attn_decode_stream_plan).  Before either, with
+ *             num_splits = 0 and more than 16 rows per KV head: when the batch alone
+ *             gives at least two workgroups per compute unit (batch * num_kv_heads *
+ *             row_groups >= 2 * CUs) and the sequences are of nearly equal length
+ *             (8 * total_kv >= 7 * batch * max_kv_len), one workgroup per (sequence,
+ *             KV head, row group) takes every chunk of its sequence in turn, as one
+ *             run, and writes the result (no partials, no merge).  Which of the three
+ *             a call uses: sink_attn_decode_plan_kind.
  *  workspace  device scratch of at least sink_attn_decode_workspace_bytes(...) bytes,
  *             256-byte aligned; contents need no initialisation.  Calls that share one
  *             workspace must be stream-ordered.
@@ -209,6 +216,20 @@ int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const 
 
 /* Bytes of the no-allocation entry point's scratch array on each GPU (its size limit). */
 size_t sink_attn_decode_noalloc_scratch_bytes(void);
+
+/* Which plan sink_attn_decode uses for these sizes (contiguous K/V), with num_cus the
+ * compute units to plan for (0 = the current device's, what sink_attn_decode uses, or 256
+ * when no device is current); -1 if the arguments are invalid. */
+typedef enum {
+  SINK_ATTN_PLAN_CHUNKS = 0,     /* chunk plan: sink_attn_decode_num_slots slots, merged
+                                    by log-sum-exp when there is more than one          */
+  SINK_ATTN_PLAN_STREAM = 1,     /* stream plan (sink_attn_decode_stream_plan)          */
+  SINK_ATTN_PLAN_WHOLE_RUNS = 2  /* every chunk of a sequence in one workgroup, which
+                                    writes the result                                  */
+} sink_attn_plan_kind;
+int32_t sink_attn_decode_plan_kind(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,
+                                   int32_t max_kv_len, int32_t num_splits, int32_t num_cus);
 
 /* Workspace bytes sink_attn_decode needs for these sizes (0 if the arguments are
  * invalid).  Holds fp32 partial outputs and partial lse for every (row, slot): S slots of
@@ -279,7 +300,9 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
  *
  * sink_attn_decode_stream_plan: 1 if the stream plan applies to these sizes (then R, the
  *   ranges per head and the slots S per row are written where the pointers are not
- *   NULL), else 0.  R is a multiple of 32, at least ceil(max_kv_len/16), so S <= 17.
+ *   NULL), else 0.  sink_attn_decode uses it unless whole-sequence runs are chosen
+ *   first (sink_attn_decode_plan_kind); the two step entry points below accept every
+ *   size it applies to.  R is a multiple of 32, at least ceil(max_kv_len/16), so S <= 17.
  *   The plan gives about 4 wavefronts (<= 16 rows) or 2 workgroups per compute unit:
  *   num_cus is the count to plan for, 0 = the current device's (what sink_attn_decode
  *   uses), or 256 when no device is current.
@@ -292,7 +315,7 @@ int sink_attn_decode_partial(const void* q, const void* k, const void* v,
  *   in `workspace` and the sinks (NULL = no sink).  A sequence with no keys gets out = 0
  *   and lse = sink (or -inf).
  * Both are exported so each step can be checked and timed; sink_attn_decode runs them
- * back to back.
+ * back to back wherever it uses the stream plan.
  */
 int32_t sink_attn_decode_stream_plan(int32_t batch, int32_t q_len, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int64_t total_kv,

@@ -307,6 +307,32 @@ def test_stream_plan_follows_cu_count(lib, cus, b, ql, hq, hkv, d, total, maxkv,
                                             None) == 0
 
 
+@pytest.mark.parametrize("cus", [256, 80, 32])
+def test_decode_plan_kind(lib, cus):
+    """sink_attn_decode picks whole-sequence runs (2) in planner mode when there are more
+    than 16 rows per KV head, at least two workgroups per CU and sequences of nearly
+    equal length; else the stream plan (1) where it applies, else the chunk plan (0)."""
+    kind = lib.sink_attn_decode_plan_kind
+    spec = (4, 64, 4, 128)                    # 64 rows per KV head, one row group
+    b = -(-2 * cus // 4)                      # the fewest sequences with 2 workgroups per CU
+    assert kind(b, *spec, b * 32768, 32768, 0, cus) == 2
+    assert kind(b - 1, *spec, (b - 1) * 32768, 32768, 0, cus) == 1     # under-filled
+    t78 = -(-7 * b * 32768 // 8)              # total at exactly 7/8 of batch * max
+    assert kind(b, *spec, t78, 32768, 0, cus) == 2
+    assert kind(b, *spec, t78 - 1, 32768, 0, cus) == 1                 # unequal lengths
+    assert kind(b, *spec, b * 32768, 32768, 32, cus) == 0              # forced chunks
+    assert kind(b, *spec, 0, 0, 0, cus) == 1                           # no keys: no runs
+    # 8 rows per KV head (the gpt-oss batch): never whole runs
+    assert kind(4 * cus, 1, 64, 8, 64, 4 * cus * 4096, 4096, 0, cus) == 1
+    # more than 64 rows per KV head (two row groups of 64): whole runs or chunks
+    assert kind(cus, 4, 128, 4, 64, cus * 4096, 4096, 0, cus) == 2
+    assert kind(cus // 8, 4, 128, 4, 64, cus // 8 * 4096, 4096, 0, cus) == 0
+    # invalid sizes
+    assert kind(0, *spec, 0, 0, 0, cus) == -1
+    assert kind(b, *spec, b * 32768, 32768, 65, cus) == -1
+    assert kind(b, *spec, b * 32768, 32768, 0, -1) == -1
+
+
 # ---------------------------------------------------------------- decode chunk plan
 def _bounds(lib, lk, ql, hq, hkv, d, ns):
     n = lib.sink_attn_decode_chunk_bounds(lk, ql, hq, hkv, d, ns, None, 0)

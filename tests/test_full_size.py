@@ -3,8 +3,10 @@ varlen prefill (8 sequences of 512..6000 tokens, 64 query heads over 8, head_dim
 the 6000-token prefill over 4 KV heads (head_dim 128, half the heads with a -inf sink),
 the chunked prefill (1024 new tokens over a 31744-token prefix, key splits from the
 planner), and all 256 sequences of the speculative decode (4 draft tokens over 32768
-keys) through both its paths: 32 chunks per sequence as the workload names them, and
-the planner's stream plan.  These are the workloads of "Hosting Qwen on Blackwell"
+keys) through its three paths: 32 chunks per sequence as the workload names them, the
+planner (whole-sequence runs: equal lengths and at least two workgroups per compute
+unit), and the stream plan's two steps on their own (equal ranges of each head's token
+axis, merged with the sinks).  These are the workloads of "Hosting Qwen on Blackwell"
 (Prefillers: ~6000-token inputs over 4 KV heads; Decoders: large batches, MTP draft
 tokens).
 
@@ -93,15 +95,21 @@ def test_chunked_prefill_full_elementwise(sa):
 
 def test_spec_decode_full_every_sequence(sa):
     """All 256 sequences, every draft token and head, through the 32-chunk path (runs of
-    chunks merged in the workgroup) and the planner's stream plan."""
+    chunks merged in the workgroup), the planner (whole-sequence runs) and the stream
+    plan's partial and merge steps (decode_stream_wg_kernel with 4 wavefronts)."""
     w = wl.make("spec_decode", device="cuda")
     tk = w.k.shape[1]
     assert w.num_splits == 32
+    assert sa.decode_plan_kind(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, w.max_kv, 0) == "whole_runs"
+    assert sa.decode_plan_kind(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, w.max_kv, 32) == "chunks"
     assert sa.decode_stream_plan(w.batch, w.q_len, w.hq, w.hkv, w.d, tk, w.max_kv) is not None
     cps = sa.decode_chunks_per_slot(w.batch, w.q_len, w.hq, w.hkv, w.d, w.max_kv, 32)
-    _say(f"spec_decode full: 32 chunks ({cps} per workgroup) and the stream plan")
+    _say(f"spec_decode full: 32 chunks ({cps} per workgroup), whole runs, stream steps")
     o32, l32 = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, 32)
-    ost, lst = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, 0)
+    owr, lwr = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, 0)
+    _, _, ws = sa.decode_stream_partial(w.q, w.k, w.v, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal)
+    ost, lst = sa.decode_stream_merge(w.sinks, w.cu_seqlens_kv, tuple(w.q.shape), tk, w.hkv,
+                                      w.max_kv, ws)
     torch.cuda.synchronize()
     ind = w.cu_seqlens_kv.cpu().tolist()
     worst = np.zeros(3)
@@ -109,7 +117,8 @@ def test_spec_decode_full_every_sequence(sa):
         ks = slice(ind[b], ind[b + 1])
         ro, rl = oracle.sink_attention_decode(w.q[b:b + 1], w.k[:, ks], w.v[:, ks], w.sinks,
                                               [0, ind[b + 1] - ind[b]], w.scale, w.causal)
-        for out, lse, what in ((o32, l32, "32 chunks"), (ost, lst, "stream plan")):
+        for out, lse, what in ((o32, l32, "32 chunks"), (owr, lwr, "whole runs"),
+                               (ost, lst, "stream steps")):
             r = _compare(out[b:b + 1], lse[b:b + 1], ro, rl, f"spec_decode {what} b={b}")
             worst = np.maximum(worst, r)
     _say(f"spec_decode full: worst max-abs {worst[0]:.2e} mean-abs {worst[1]:.2e} lse {worst[2]:.2e}")

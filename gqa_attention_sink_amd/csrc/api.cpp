@@ -36,7 +36,8 @@ inline bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 //  - otherwise the split kernel streams a run of consecutive chunks in turn.  With a
 //    forced chunk count the run is as long as keeps about four workgroups per compute
 //    unit (two rounds of the two that fit), so long runs stream unbroken and few
-//    partials are written; in planner mode the run is one chunk.
+//    partials are written; in planner mode the run is one chunk (sink_attn_decode may
+//    instead give one workgroup every chunk of its sequence: whole_runs below).
 // slots = ceil(n_max / chunks per slot), n_max the chunk count at max_kv_len (the plan
 // is nondecreasing in the length).
 constexpr int kRunWgsPerCu = 4;

@@ -265,20 +265,23 @@ def test_decode_cases(sa, case):
     _compare(out, lse, ro, rl, f"decode case {case}")
 
 
-@pytest.mark.parametrize("ql,hq,hkv,d", [(4, 32, 2, 128), (3, 48, 4, 64)])
+@pytest.mark.parametrize("ql,hq,hkv,d", [(4, 32, 2, 128), (3, 48, 4, 64), (1, 64, 2, 128),
+                                         (4, 64, 2, 64)])
 def test_decode_whole_runs_match_oracle(sa, ql, hq, hkv, d):
     """Planner mode with whole-sequence runs (more than 16 rows per KV head, at least two
     workgroups per compute unit, lengths within 7/8 of the longest on average): every
     sequence against the oracle, with an empty sequence and lengths off the 32-key
     stages."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    batch = -(-2 * cus // hkv)
-    rng = np.random.default_rng(300 + d)
+    rows = ql * (hq // hkv)                    # 36..128 rows: 2 or 4 wavefronts, 1 or 2 groups
+    row_groups = -(-rows // 64)
+    batch = -(-2 * cus // (hkv * row_groups))
+    rng = np.random.default_rng(300 + d + rows)
     lens = [int(x) for x in rng.integers(460, 513, batch)]
     lens[1], lens[2] = 0, 512
     _say(f"whole runs: batch={batch} q_len={ql} hq={hq} hkv={hkv} d={d}")
     w = wl.make_decode(lens, ql, hq, hkv, d, ("normal", 0, 2), 1 / math.sqrt(d), True, 0,
-                       seed=300 + d, device="cuda")
+                       seed=300 + d + rows, device="cuda")
     assert sa.decode_plan_kind(batch, ql, hq, hkv, d, w.k.shape[1], w.max_kv, 0) == "whole_runs"
     out, lse = _run_decode(sa, w, 0)
     torch.cuda.synchronize()

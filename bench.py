@@ -588,7 +588,7 @@ def main():
                          "kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(decode shards by sequence and prefill by head with no exchange inside "
               "attention); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)

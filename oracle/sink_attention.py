@@ -14,7 +14,7 @@ sink is included in the first block only.  The same page's "model deltas" list s
 every attention head owns one pre-trained sink parameter that takes part in the
 softmax, and that attention is grouped-query (GQA).
 
-Readings of points the pages leave open (each is also recorded in the design doc):
+Readings of points the pages leave open:
 
 * The sink is one extra logit column with no value row.  Adding the same scalar to
   every logit would be a no-op under softmax, so the only reading that changes the

@@ -7,8 +7,7 @@ may call it.  It shares no code with the HIP kernels.
 "GPT-OSS on day 0" (*model deltas*) says only that the model uses YaRN position
 encoding as DeepSeek-V3 does.  The computation below is the published YaRN method
 (rotary embedding with "NTK-by-parts" frequency interpolation and an attention
-temperature), restated; every choice the pages leave open is a reading, also listed in
-DESIGN.md:
+temperature), restated; every choice the pages leave open is a reading:
 
 * rotary frequencies of a head of size D: f_i = theta ** (-2 i / D), i = 0 .. D/2 - 1;
 * YaRN interpolation with scale factor s over an original context L: a frequency with

@@ -265,9 +265,14 @@ def test_decode_cases(sa, case):
     _compare(out, lse, ro, rl, f"decode case {case}")
 
 
-@pytest.mark.parametrize("ql,hq,hkv,d", [(4, 32, 2, 128), (3, 48, 4, 64), (1, 64, 2, 128),
-                                         (4, 64, 2, 64)])
-def test_decode_whole_runs_match_oracle(sa, ql, hq, hkv, d):
+@pytest.mark.parametrize("ql,hq,hkv,d,sink,causal", [
+    (4, 32, 2, 128, ("normal", 0, 2), True),
+    (3, 48, 4, 64, ("normal", 0, 2), True),
+    (1, 64, 2, 128, ("normal", 0, 2), True),
+    (4, 64, 2, 64, ("normal", 0, 2), True),
+    (2, 32, 2, 128, ("alt_neginf", 2, 1), False),   # -inf sinks on half the heads, no mask
+])
+def test_decode_whole_runs_match_oracle(sa, ql, hq, hkv, d, sink, causal):
     """Planner mode with whole-sequence runs (more than 16 rows per KV head, at least two
     workgroups per compute unit, lengths within 7/8 of the longest on average): every
     sequence against the oracle, with an empty sequence and lengths off the 32-key
@@ -280,7 +285,7 @@ def test_decode_whole_runs_match_oracle(sa, ql, hq, hkv, d):
     lens = [int(x) for x in rng.integers(460, 513, batch)]
     lens[1], lens[2] = 0, 512
     _say(f"whole runs: batch={batch} q_len={ql} hq={hq} hkv={hkv} d={d}")
-    w = wl.make_decode(lens, ql, hq, hkv, d, ("normal", 0, 2), 1 / math.sqrt(d), True, 0,
+    w = wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, 0,
                        seed=300 + d + rows, device="cuda")
     assert sa.decode_plan_kind(batch, ql, hq, hkv, d, w.k.shape[1], w.max_kv, 0) == "whole_runs"
     out, lse = _run_decode(sa, w, 0)

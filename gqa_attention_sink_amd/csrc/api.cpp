@@ -107,7 +107,7 @@ sa::StreamPlan stream_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t hkv
   p.num_kv_heads = hkv;
   return p;
 }
-// Whole-sequence runs (planner mode, contiguous K/V, more than 16 rows per KV head): when
+// Whole-sequence runs (planner mode, more than 16 rows per KV head): when
 // the batch alone gives at least kWholeRunWgsPerCu workgroups per compute unit and the
 // sequences are of nearly equal length (total_kv >= 7/8 of batch * max_kv_len), one
 // workgroup per (sequence, KV head, row group) streams every chunk of its sequence in
@@ -241,15 +241,18 @@ int run_decode(sa::DecodeArgs& a, int32_t batch, int32_t q_len, int32_t num_q_he
   hipStream_t st = (hipStream_t)stream;
   // A paged cache streams along its page list laid end to end (single-wavefront plans).
   const bool paged = page_ids != nullptr;
-  if (!paged && whole_runs(batch, q_len, num_q_heads, num_kv_heads, a.total_kv, max_kv_len,
-                           num_splits, resolve_cus(0))) {
+  // tokens on the key axis: a paged cache's list of n pages holds more than
+  // (n - batch) * page_size of them
+  const int64_t tokens = paged ? (a.num_page_entries - batch) * (int64_t)a.page_size : a.total_kv;
+  if (whole_runs(batch, q_len, num_q_heads, num_kv_heads, tokens, max_kv_len, num_splits,
+                 resolve_cus(0))) {
     // one slot holding every chunk of the plan at max_kv_len (a sequence's own plan has
     // no more chunks): the split kernel writes the result
     a.chunk_run = sa::plan_chunks(max_kv_len, 0, 1);
     a.num_slots = 1;
     a.out = out;
     a.lse = lse;
-    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, nullptr, rope, st);
+    hipError_t e = sa::launch_decode_split(a, head_dim, batch, num_kv_heads, true, page_ids, rope, st);
     if (e != hipSuccess) return hip_fail(e);
     return SINK_ATTN_OK;
   }

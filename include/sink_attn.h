@@ -217,9 +217,12 @@ int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const 
 /* Bytes of the no-allocation entry point's scratch array on each GPU (its size limit). */
 size_t sink_attn_decode_noalloc_scratch_bytes(void);
 
-/* Which plan sink_attn_decode uses for these sizes (contiguous K/V), with num_cus the
- * compute units to plan for (0 = the current device's, what sink_attn_decode uses, or 256
- * when no device is current); -1 if the arguments are invalid. */
+/* Which plan sink_attn_decode uses for these sizes, with num_cus the compute units to plan
+ * for (0 = the current device's, what sink_attn_decode uses, or 256 when no device is
+ * current); -1 if the arguments are invalid.  sink_attn_decode_paged makes the same choice
+ * between whole-sequence runs and the chunk plan with total_kv taken as
+ * (num_page_entries - batch) * page_size, a lower bound of the tokens its page list
+ * holds (it has no stream plan above 16 rows per KV head). */
 typedef enum {
   SINK_ATTN_PLAN_CHUNKS = 0,     /* chunk plan: sink_attn_decode_num_slots slots, merged
                                     by log-sum-exp when there is more than one          */
@@ -372,7 +375,10 @@ int sink_attn_merge(const float* part_o, const float* part_lse, const int32_t* s
 
 /* Decode over a paged cache; every other argument and the workspace are as for
  * sink_attn_decode (workspace size from sink_attn_decode_workspace_bytes).  max_kv_len
- * is a host upper bound of L_b. */
+ * is a host upper bound of L_b.  Plans: in planner mode at most 16 rows per KV head take
+ * the stream plan along the page list laid end to end; more rows take whole-sequence
+ * runs when sink_attn_decode_plan_kind's rule holds with total_kv =
+ * (num_page_entries - batch) * page_size, else the chunk plan. */
 int sink_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                            const float* sinks, const int32_t* kv_page_indptr,
                            const int32_t* kv_page_indices, const int32_t* kv_last_page_len,

@@ -152,6 +152,37 @@ def test_paged_stream_equals_contiguous_stream_bitwise(sa, ps, d, ql, hq, hkv):
     assert torch.equal(op.reshape(oc.shape), oc) and torch.equal(lp.reshape(lc.shape), lc)
 
 
+@pytest.mark.parametrize("ps,d,ql,hq,hkv", [(16, 128, 4, 32, 2), (48, 64, 3, 48, 4)])
+def test_paged_whole_runs_equal_contiguous_bitwise(sa, ps, d, ql, hq, hkv):
+    """Planner mode with more than 16 rows per KV head and a batch of nearly equal
+    lengths that gives two workgroups per compute unit: paged and contiguous decode both
+    take whole-sequence runs, the same chunks of every sequence in the same order, so
+    they agree bit for bit (and with the oracle), although the pages are scattered and
+    unused slots hold NaN."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    batch = -(-2 * cus // hkv)
+    g = torch.Generator().manual_seed(650 + ps)
+    lens = (480 + torch.randint(0, 33, (batch,), generator=g)).tolist()
+    lens[3] = 0
+    w = wl.make_decode(lens, ql, hq, hkv, d, ("normal", 0, 2), 1 / math.sqrt(d), True, 0,
+                       seed=660 + ps, device="cuda")
+    pk = wl.make_paged(w, ps, seed=661 + ps, fill="nan")
+    entries = pk.kv_page_indices.numel()
+    assert sa.decode_plan_kind(batch, ql, hq, hkv, d, (entries - batch) * ps, w.max_kv, 0) \
+        == "whole_runs"
+    assert sa.decode_plan_kind(batch, ql, hq, hkv, d, w.k.shape[1], w.max_kv, 0) == "whole_runs"
+    _say(f"paged vs contiguous whole runs ps={ps} d={d} batch={batch}")
+    op, lp = _run(sa, w, pk)
+    oc, lc = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale, w.causal, 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(op.float()).all()
+    assert torch.equal(op.reshape(oc.shape), oc) and torch.equal(lp.reshape(lc.shape), lc)
+    ro, rl = oracle.sink_attention_decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv.cpu(),
+                                          w.scale, w.causal)
+    err = np.abs(op.float().cpu().numpy().astype(np.float64).reshape(ro.shape) - ro)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
 @pytest.mark.parametrize("ps,d", [(16, 64), (48, 128), (256, 64)])
 def test_kv_append_bitwise(sa, ps, d):
     """Append 1..37 new tokens per sequence into a scattered paged cache; the whole caches

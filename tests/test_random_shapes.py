@@ -1,0 +1,122 @@
+"""GPU parity on seeded random shapes: decode over contiguous and paged caches (every plan
+the library picks for them: chunk runs, stream ranges, forced chunk counts) and prefill
+with and without key splits, against the fp64 oracle.
+
+Each case draws its batch, draft length, GQA group, KV heads, head_dim, per-sequence
+lengths (some empty, some a single key, ragged against the 32-key stages and the
+pages), sink kind, causal flag and chunk count from its own seed, so a failure names a
+case that reruns alone.  Tolerances as everywhere: out max-abs <= 2e-2 and mean-abs
+<= 2e-3, lse within 1e-3, -inf lse entries exactly.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gqa_attention_sink_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, LSE_TOL = 2e-2, 2e-3, 1e-3
+SINKS = [("normal", 0, 2), ("alt_neginf", 2, 1), None, ("normal", 6, 1)]
+
+
+def _say(msg):
+    print(f"[random] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sink_amd as pkg
+    pkg.load()
+    return pkg
+
+
+def _compare(out, lse, ref_out, ref_lse, what):
+    o = out.detach().float().cpu().numpy().astype(np.float64).reshape(ref_out.shape)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err = np.abs(o - ref_out)
+    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean-abs {err.mean():.3e}"
+    l = lse.detach().float().cpu().numpy().astype(np.float64).reshape(ref_lse.shape)
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_lse)), f"{what}: -inf lse pattern"
+    fin = np.isfinite(ref_lse)
+    if fin.any():
+        le = np.abs(l[fin] - ref_lse[fin]).max()
+        assert le <= LSE_TOL, f"{what}: lse err {le:.3e}"
+
+
+def _decode_case(i):
+    r = np.random.default_rng(900 + i)
+    ql = int(r.integers(1, 5))
+    group = int(r.choice([1, 2, 4, 6, 8, 16]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    d = int(r.choice([64, 128]))
+    batch = int(r.integers(1, 10))
+    lens = [int(x) for x in r.integers(ql, 2600, batch)]
+    ns = int(r.choice([0, 0, 0, 1, 3, 7, 16]))
+    sink = SINKS[int(r.integers(0, len(SINKS)))]
+    causal = bool(r.integers(0, 4) > 0)
+    if batch > 2:  # an empty sequence, or one with as many keys as draft tokens (or 1)
+        lens[int(r.integers(0, batch))] = int(r.choice([0, ql] if causal else [0, 1, ql]))
+    page = int(r.choice([0, 0, 16, 32, 64, 128]))   # 0: contiguous cache
+    return lens, ql, group * hkv, hkv, d, sink, causal, ns, page
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_decode(sa, i):
+    lens, ql, hq, hkv, d, sink, causal, ns, page = _decode_case(i)
+    w = wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, ns,
+                       seed=950 + i, device="cuda")
+    kind = sa.decode_plan_kind(len(lens), ql, hq, hkv, d, w.k.shape[1], w.max_kv, ns)
+    _say(f"decode {i}: lens={lens} q_len={ql} hq={hq} hkv={hkv} d={d} splits={ns} "
+         f"sink={sink} causal={causal} page={page} plan={kind}")
+    if page:
+        pk = wl.make_paged(w, page, seed=960 + i, fill="nan")
+        out, lse = sa.decode_paged(w.q, pk.k_cache, pk.v_cache, w.sinks, pk.kv_page_indptr,
+                                   pk.kv_page_indices, pk.kv_last_page_len, w.max_kv, w.scale,
+                                   w.causal, ns)
+    else:
+        out, lse = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                             w.causal, ns)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sink_attention_decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv.cpu(),
+                                          w.scale, w.causal)
+    _compare(out, lse, ro, rl, f"decode case {i}")
+
+
+def _prefill_case(i):
+    r = np.random.default_rng(1900 + i)
+    group = int(r.choice([1, 2, 3, 4, 8, 16]))
+    hkv = int(r.choice([1, 2, 4]))
+    d = int(r.choice([64, 128]))
+    batch = int(r.integers(1, 5))
+    lens_q = [int(x) for x in r.integers(1, 700, batch)]
+    prefix = [int(x) for x in r.integers(0, 600, batch)] if r.integers(0, 2) else [0] * batch
+    lens_kv = [a + b for a, b in zip(lens_q, prefix)]
+    ns = int(r.choice([1, 1, 0, 2, 5]))
+    sink = SINKS[int(r.integers(0, len(SINKS)))]
+    causal = bool(r.integers(0, 4) > 0)
+    return lens_q, lens_kv, group * hkv, hkv, d, sink, causal, ns
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_prefill(sa, i):
+    lens_q, lens_kv, hq, hkv, d, sink, causal, ns = _prefill_case(i)
+    _say(f"prefill {i}: lens_q={lens_q} lens_kv={lens_kv} hq={hq} hkv={hkv} d={d} "
+         f"splits={ns} sink={sink} causal={causal}")
+    w = wl.make_prefill(lens_q, lens_kv, hq, hkv, d, sink, 1 / math.sqrt(d), causal,
+                        seed=1950 + i, device="cuda")
+    out, lse = sa.prefill(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q, w.cu_seqlens_kv,
+                          max(lens_q), w.scale, w.causal, num_splits=ns,
+                          max_seqlen_kv=max(lens_kv))
+    torch.cuda.synchronize()
+    ro, rl = oracle.sink_attention(w.q, w.k, w.v, w.sinks, w.cu_seqlens_q.cpu(),
+                                   w.cu_seqlens_kv.cpu(), w.scale, w.causal)
+    _compare(out, lse, ro, rl, f"prefill case {i}")

@@ -60,16 +60,19 @@ def _decode_case(i):
     d = int(r.choice([64, 128]))
     batch = int(r.integers(1, 10))
     lens = [int(x) for x in r.integers(ql, 2600, batch)]
-    ns = int(r.choice([0, 0, 0, 1, 3, 7, 16]))
+    ns = int(r.choice([0, 0, 0, 0, 1, 3, 7, 16]))
     sink = SINKS[int(r.integers(0, len(SINKS)))]
     causal = bool(r.integers(0, 4) > 0)
     if batch > 2:  # an empty sequence, or one with as many keys as draft tokens (or 1)
         lens[int(r.integers(0, batch))] = int(r.choice([0, ql] if causal else [0, 1, ql]))
-    page = int(r.choice([0, 0, 16, 32, 64, 128]))   # 0: contiguous cache
+    page = int(r.choice([0, 0, 0, 0, 16, 32, 64, 128]))   # 0: contiguous cache
+    if i >= 40:  # the stream plan's workgroup kernel: planner, contiguous, 16 < rows <= 64
+        ql, page, ns = 4, 0, 0
+        group = [6, 8, 16, 16][i - 40]
     return lens, ql, group * hkv, hkv, d, sink, causal, ns, page
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(44))
 def test_random_decode(sa, i):
     lens, ql, hq, hkv, d, sink, causal, ns, page = _decode_case(i)
     w = wl.make_decode(lens, ql, hq, hkv, d, sink, 1 / math.sqrt(d), causal, ns,

@@ -414,7 +414,7 @@ def prefill_line(sa, w, steps, warmup, flush, cpu_budget, num_splits=1):
     kname = "prefill_kernel" if w.d == 64 else "prefill_pp_kernel"
     # HBM bytes if every tensor moved once: Q, K, V read, O and lse written
     min_bytes = 2 * tq * w.hq * w.d * 2 + 2 * tk * w.hkv * w.d * 2 + tq * w.hq * 4
-    traffic = _traffic_for(kname, w.name) if ns == 1 else None
+    traffic = _traffic_for(kname, w.name)   # the prefill kernel's launch (not the merge)
     line = {"TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "ms": _r(whole["median"]), "ms_min": _r(whole["min"]), "ms_mean": _r(whole["mean"]),
             "steps": whole["n"], "flops": fl, "key_splits": ns, "min_hbm_bytes": min_bytes,
@@ -461,8 +461,11 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
                                  (" with fused YaRN rotation of q" if rope else ""),
                      "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel (paged)",
                                   "achieved": round(g, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(g / HBM_PEAK_GBS, 4), "traffic": None,
-                                  "note": "whole call (stream kernel + merge)"}}
+                                  "frac": round(g / HBM_PEAK_GBS, 4),
+                                  "traffic": None if rope else _traffic_for(
+                                      "decode_stream_kernel_paged", "decode_gptoss_paged16"),
+                                  "note": "whole call (stream kernel + merge); traffic: the "
+                                          "stream kernel's launch"}}
         if rope:
             res[name]["rope"] = YARN_BENCH
     if cpu_budget:
@@ -489,7 +492,9 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
                                  (" with fused YaRN rotation of the keys" if rope else ""),
                      "roofline": {"bound": "hbm", "kernel": "kv_append_kernel",
                                   "achieved": round(g, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(g / HBM_PEAK_GBS, 4), "traffic": None}}
+                                  "frac": round(g / HBM_PEAK_GBS, 4),
+                                  "traffic": None if rope else _traffic_for("kv_append_kernel",
+                                                                            "kv_append")}}
     if cpu_budget:
         res["kv_append"]["cpu_baseline"] = cpu_append(p, pk, k_new, v_new, 16, cpu_budget)
         res["kv_append_rope"]["cpu_baseline"] = cpu_append(p, pk, k_new, v_new, 16, cpu_budget,

@@ -699,8 +699,11 @@ int sink_attn_decode_noalloc(const void* q, const void* k, const void* v, const 
     if (batch > 65535) return SINK_ATTN_ERR_UNSUPPORTED;
     sa::RopeArgs ra;
     if (make_rope(rope, head_dim, &ra) != SINK_ATTN_OK) return SINK_ATTN_ERR_INVALID_ARG;
-    // the workspace sink_attn_decode would need must fit the scratch array
-    if (sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+    // the workspace sink_attn_decode would need must fit the scratch array, unless the
+    // call takes whole-sequence runs, which write no partials
+    if (!whole_runs(batch, q_len, num_q_heads, num_kv_heads, total_kv, max_kv_len, num_splits,
+                    resolve_cus(0)) &&
+        sink_attn_decode_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim,
                                          max_kv_len, num_splits) > sa::kNoAllocScratchBytes)
       return SINK_ATTN_ERR_SCRATCH_LIMIT;
     void* scratch = nullptr;

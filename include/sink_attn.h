@@ -197,9 +197,12 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
  * workspace.  Nothing is allocated or freed by the call.
  *  - Limit: inputs whose sink_attn_decode_workspace_bytes(...) exceeds
  *    sink_attn_decode_noalloc_scratch_bytes() (32 MiB) are rejected with
- *    SINK_ATTN_ERR_SCRATCH_LIMIT before any HIP call.  (The gpt-oss-like batch of 64
- *    sequences up to 8192 keys, 64 query heads over 8, fits; a 256-sequence
- *    speculative-decode batch does not: use sink_attn_decode with a workspace.)
+ *    SINK_ATTN_ERR_SCRATCH_LIMIT before any HIP call, unless sink_attn_decode_plan_kind
+ *    reports whole-sequence runs, which write no partials.  (The gpt-oss-like batch of 64
+ *    sequences up to 8192 keys, 64 query heads over 8, fits; so does the 256-sequence
+ *    speculative-decode batch of equal lengths, through whole-sequence runs on a 256-CU
+ *    MI355X; a multi-token batch of unequal lengths with that many rows does not: use
+ *    sink_attn_decode with a workspace.)
  *  - Each GPU holds its own copy of the array from the library's load until the process
  *    ends; its device address is looked up on the first call with that GPU current.
  *  - Every call on one GPU shares that GPU's array and it keeps the last call's

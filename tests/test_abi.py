@@ -425,7 +425,8 @@ def test_kv_append_rejects_misaligned(lib):
 
 def test_decode_noalloc_validation(lib):
     """The no-allocation decode validates like sink_attn_decode and rejects inputs whose
-    workspace would exceed its scratch array, all before any HIP call."""
+    workspace would exceed its scratch array (unless they take whole-sequence runs, which
+    write no partials), all before any HIP call."""
     f = lib.sink_attn_decode_noalloc
     assert lib.sink_attn_decode_noalloc_scratch_bytes() == 32 << 20
     def call(**kw):
@@ -434,8 +435,9 @@ def test_decode_noalloc_validation(lib):
         a.update(kw)
         return f(a["q"], FAKE, FAKE, None, a["ind"], a["batch"], a["ql"], a["tk"], a["maxk"],
                  a["hq"], a["hkv"], a["d"], 0.088, 1, a["ns"], a["out"], None, None, None)
-    assert call() == 6                                   # speculative-decode batch: too large
-    assert call(ns=0) == 6
+    assert call() == 6                                   # 32 forced chunks: too large
+    assert call(ns=0) != 6                               # planner: whole-sequence runs
+    assert call(ns=0, tk=200 * 32768) == 6               # unequal lengths: stream partials
     assert call(q=None) == INVALID and call(out=None) == INVALID and call(ind=None) == INVALID
     assert call(ql=5) == UNSUPPORTED and call(hq=63) == INVALID and call(ns=65) == INVALID
     assert b"SCRATCH_LIMIT" in lib.sink_attn_status_str(6)

@@ -75,6 +75,34 @@ def test_noalloc_matches_decode_twice(sa, case):
         _check_against_decode(sa, w, ns)
 
 
+def test_noalloc_whole_runs_need_no_scratch(sa):
+    """A batch that takes whole-sequence runs needs more than the array as a workspace for
+    the other plans, yet runs: those runs write no partials.  Bit for bit against
+    sink_attn_decode, then a smaller call through the array."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    batch = -(-2 * cus // 2)
+    g = torch.Generator().manual_seed(960)
+    lens = (480 + torch.randint(0, 33, (batch,), generator=g)).tolist()
+    w = wl.make_decode(lens, 4, 32, 2, 128, ("normal", 0, 2), 1 / math.sqrt(128), True, 0,
+                       seed=961, device="cuda")
+    assert sa.decode_plan_kind(batch, 4, 32, 2, 128, w.k.shape[1], w.max_kv, 0) == "whole_runs"
+    assert sa.decode_workspace_bytes(batch, 4, 32, 2, 128, w.max_kv, 0) > \
+        sa.decode_noalloc_scratch_bytes()
+    _say(f"whole runs through the no-allocation entry point: batch={batch}")
+    ref_out, ref_lse = sa.decode(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, w.scale,
+                                 True, 0)
+    out = torch.full_like(w.q, float("nan"))
+    lse = torch.full((batch, 4, 32), float("nan"), dtype=torch.float32, device="cuda")
+    sa.decode_noalloc(w.q, w.k, w.v, w.sinks, w.cu_seqlens_kv, w.max_kv, out, lse, w.scale,
+                      True, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+    small = wl.make_decode([300, 2000, 7], 1, 64, 8, 64, ("normal", 0, 2), 0.125, True, 0,
+                           seed=962, device="cuda")
+    _check_against_decode(sa, small, 0)
+
+
 def test_noalloc_rejects_oversize(sa):
     """64 sequences of 4 draft tokens over 64 query heads (16384 rows) need a 142 MB
     workspace, more than the array holds: a clear error before any launch, and the

@@ -16,6 +16,7 @@ HEADER = os.path.join(ROOT, "include", "sink_attn.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+# or has nothing to compute, so none of them launches a kernel
 
 
 @pytest.fixture(scope="module")
@@ -425,8 +426,9 @@ def test_kv_append_rejects_misaligned(lib):
 
 def test_decode_noalloc_validation(lib):
     """The no-allocation decode validates like sink_attn_decode and rejects inputs whose
-    workspace would exceed its scratch array (unless they take whole-sequence runs, which
-    write no partials), all before any HIP call."""
+    workspace would exceed its scratch array, all before any kernel launch.  A batch that
+    takes whole-sequence runs writes no partials and is not rejected; it would launch, so
+    here only its plan is checked (the GPU tests run it)."""
     f = lib.sink_attn_decode_noalloc
     assert lib.sink_attn_decode_noalloc_scratch_bytes() == 32 << 20
     def call(**kw):
@@ -436,7 +438,8 @@ def test_decode_noalloc_validation(lib):
         return f(a["q"], FAKE, FAKE, None, a["ind"], a["batch"], a["ql"], a["tk"], a["maxk"],
                  a["hq"], a["hkv"], a["d"], 0.088, 1, a["ns"], a["out"], None, None, None)
     assert call() == 6                                   # 32 forced chunks: too large
-    assert call(ns=0) != 6                               # planner: whole-sequence runs
+    assert lib.sink_attn_decode_plan_kind(256, 4, 64, 4, 128, 256 * 32768, 32768, 0,
+                                          256) == 2      # planner: whole-sequence runs
     assert call(ns=0, tk=200 * 32768) == 6               # unequal lengths: stream partials
     assert call(q=None) == INVALID and call(out=None) == INVALID and call(ind=None) == INVALID
     assert call(ql=5) == UNSUPPORTED and call(hq=63) == INVALID and call(ns=65) == INVALID

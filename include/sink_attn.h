@@ -27,7 +27,8 @@
  *    (ln(e^sink + sum_j e^(s_j))); -inf for a row with no key and no sink.
  *  - A NULL `sinks` means no sink (every sink = -inf).  A sink may be -inf per head.
  *  - Return value: a sink_attn_status.  Every precondition that the host can check is
- *    checked before any HIP call; device-side preconditions (monotone index arrays,
+ *    checked before any kernel launch (the only HIP calls before then read the device's
+ *    compute-unit count); device-side preconditions (monotone index arrays,
  *    offsets within the totals) are documented, not checked, because checking them
  *    would need a synchronisation -- but every device read of K, V and Q goes through
  *    bounded buffer loads, so a violation yields wrong numbers, never a fault.
@@ -197,7 +198,7 @@ int sink_attn_decode(const void* q, const void* k, const void* v, const float* s
  * workspace.  Nothing is allocated or freed by the call.
  *  - Limit: inputs whose sink_attn_decode_workspace_bytes(...) exceeds
  *    sink_attn_decode_noalloc_scratch_bytes() (32 MiB) are rejected with
- *    SINK_ATTN_ERR_SCRATCH_LIMIT before any HIP call, unless sink_attn_decode_plan_kind
+ *    SINK_ATTN_ERR_SCRATCH_LIMIT before any kernel launch, unless sink_attn_decode_plan_kind
  *    reports whole-sequence runs, which write no partials.  (The gpt-oss-like batch of 64
  *    sequences up to 8192 keys, 64 query heads over 8, fits; so does the 256-sequence
  *    speculative-decode batch of equal lengths, through whole-sequence runs on a 256-CU

@@ -439,7 +439,26 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
     seeded permutation) and the KV append of the varlen batch's K/V into a paged cache.
     Bytes are algorithmic: decode as the contiguous decode plus the page list; append =
     new K and V read once and written once."""
+    from gqa_attention_sink_amd import sink_attn as sam
     from gqa_attention_sink_amd import workloads as wl
+    lib = sam.load()
+    P = sam._ptr
+    st = sam._stream(torch.device("cuda"))
+
+    def paged_call(w, pk, ws, out, lse, rope):
+        """sink_attn_decode_paged with its arguments marshalled once (checked by one
+        call through the binding first)."""
+        sa.decode_paged(w.q, pk.k_cache, pk.v_cache, w.sinks, pk.kv_page_indptr,
+                        pk.kv_page_indices, pk.kv_last_page_len, w.max_kv, w.scale, w.causal,
+                        w.num_splits, workspace=ws, out=out, lse=lse, rope=rope)
+        npg, hkv, ps, d = pk.k_cache.shape[0], pk.k_cache.shape[1], pk.k_cache.shape[2], w.d
+        return _c_call(lib.sink_attn_decode_paged,
+                       (P(w.q), P(pk.k_cache), P(pk.v_cache), P(w.sinks), P(pk.kv_page_indptr),
+                        P(pk.kv_page_indices), P(pk.kv_last_page_len), w.batch, w.q_len,
+                        pk.kv_page_indices.numel(), npg, ps, int(w.max_kv), w.hq, hkv, d,
+                        float(w.scale), int(bool(w.causal)), int(w.num_splits), P(ws), ws.numel(),
+                        P(out), P(lse), None if rope is None else ctypes.byref(rope), st))
+
     res = {}
     w = wl.make("decode_gptoss", device="cuda")
     pk = wl.make_paged(w, 16, seed=4242)
@@ -448,10 +467,7 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
     lse = torch.empty((w.batch, w.q_len, w.hq), dtype=torch.float32, device="cuda")
     nbytes = decode_bytes(w) + pk.kv_page_indices.numel() * 4 + w.batch * 4
     for name, rope in (("paged_decode", None), ("paged_decode_rope", sa.RopeParams(**YARN_BENCH))):
-        fn = lambda: sa.decode_paged(w.q, pk.k_cache, pk.v_cache, w.sinks, pk.kv_page_indptr,  # noqa: E731
-                                     pk.kv_page_indices, pk.kv_last_page_len, w.max_kv, w.scale,
-                                     w.causal, w.num_splits, workspace=ws, out=out, lse=lse,
-                                     rope=rope)
+        fn = paged_call(w, pk, ws, out, lse, rope)
         s, _ = time_calls([fn], steps, warmup, flush)
         g = nbytes / (s["median"] * 1e-3) / 1e9
         res[name] = {"GB/s": round(g, 2), "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4),
@@ -473,6 +489,36 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
         res["paged_decode_rope"]["cpu_baseline"] = cpu_paged(w, pk, 16, cpu_budget, YARN_BENCH)
     del pk, ws
     torch.cuda.empty_cache()
+    # the speculative-decode batch in 16-token pages, planner mode
+    w5 = wl.make("spec_decode", device="cuda")
+    w5.num_splits = 0
+    pk5 = wl.make_paged(w5, 16, seed=4242)
+    w5.k = w5.v = None  # only the paged copy is read
+    torch.cuda.empty_cache()
+    kind = sa.decode_plan_kind(w5.batch, w5.q_len, w5.hq, w5.hkv, w5.d,
+                               (pk5.kv_page_indices.numel() - w5.batch) * 16, w5.max_kv, 0)
+    ws5 = sa.decode_workspace(w5.batch, w5.q_len, w5.hq, w5.hkv, w5.d, w5.max_kv, 0)
+    out5 = torch.empty_like(w5.q)
+    lse5 = torch.empty((w5.batch, w5.q_len, w5.hq), dtype=torch.float32, device="cuda")
+    s, _ = time_calls([paged_call(w5, pk5, ws5, out5, lse5, None)], steps, warmup, flush)
+    nb5 = decode_bytes(w5) + pk5.kv_page_indices.numel() * 4 + w5.batch * 4
+    g = nb5 / (s["median"] * 1e-3) / 1e9
+    kname = "decode_split_kernel" if kind == "whole_runs" else "decode_stream_wg_kernel"
+    res["paged_spec_decode"] = {
+        "GB/s": round(g, 2), "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4),
+        "ms": _r(s["median"]), "ms_min": _r(s["min"]), "ms_mean": _r(s["mean"]),
+        "steps": s["n"], "page_size": 16, "bytes": nb5, "plan": kind,
+        "workload": "spec_decode in a paged cache, planner mode (num_splits = 0)",
+        "roofline": {"bound": "hbm", "kernel": kname + " (paged)", "achieved": round(g, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic_for(kname + "_paged", "spec_decode_paged16"),
+                     "note": "whole call (one kernel: every chunk of a sequence in one "
+                             "workgroup, the result written directly)"
+                             if kind == "whole_runs" else "whole call"}}
+    if cpu_budget:
+        res["paged_spec_decode"]["cpu_baseline"] = cpu_paged(w5, pk5, 16, cpu_budget)
+    del w5, pk5, ws5, out5, lse5
+    torch.cuda.empty_cache()
     p = wl.make("varlen_prefill", device="cuda")
     pk = wl.make_paged(p, 16, seed=4343)
     k_new = p.k.permute(1, 0, 2).contiguous()
@@ -480,8 +526,14 @@ def paged_lines(sa, steps, warmup, flush, cpu_budget):
     app = p.cu_seqlens_kv
     nbytes = 2 * 2 * k_new.numel() * 2
     for name, rope in (("kv_append", None), ("kv_append_rope", sa.RopeParams(**YARN_BENCH))):
-        fn = lambda: sa.kv_append(k_new, v_new, app, pk.kv_page_indptr, pk.kv_page_indices,  # noqa: E731
-                                  pk.kv_last_page_len, pk.k_cache, pk.v_cache, p.max_kv, rope=rope)
+        sa.kv_append(k_new, v_new, app, pk.kv_page_indptr, pk.kv_page_indices,
+                     pk.kv_last_page_len, pk.k_cache, pk.v_cache, p.max_kv, rope=rope)
+        fn = _c_call(lib.sink_attn_kv_append,
+                     (P(k_new), P(v_new), P(app), P(pk.kv_page_indptr), P(pk.kv_page_indices),
+                      P(pk.kv_last_page_len), p.batch, int(p.max_kv), k_new.shape[0],
+                      pk.kv_page_indices.numel(), pk.k_cache.shape[0], 16, p.hkv, p.d,
+                      P(pk.k_cache), P(pk.v_cache), None if rope is None else ctypes.byref(rope),
+                      st))
         s, _ = time_calls([fn], steps, warmup, flush)
         g = nbytes / (s["median"] * 1e-3) / 1e9
         res[name] = {"GB/s": round(g, 2), "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4),

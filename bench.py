@@ -575,9 +575,10 @@ def tiny_line(sa, steps, warmup, flush, cpu_budget):
 def peaks(w, steps, warmup, flush):
     """Achievable rates measured on this GPU: a flat non-temporal read of the headline's
     K and V (the same bytes, one launch each, every workgroup streaming one contiguous
-    share), a register-only bf16 MFMA loop with two wavefronts per SIMD, and the MFMA rate
+    share), a register-only bf16 MFMA loop with two wavefronts per SIMD, the MFMA rate
     of one chain per SIMD beside 0-4 exp2+FMA pairs per MFMA (the softmax's vector work)
-    issued by the same wavefront or by the other wavefront of the SIMD."""
+    issued by the same wavefront or by the other wavefront of the SIMD, and the issue rate
+    of v_exp_f32 and v_fma_f32 with 1, 2 or 4 wavefronts per SIMD."""
     from gqa_attention_sink_amd import build as bld
     lib = ctypes.CDLL(bld.PEAK_LIB)
     lib.sink_attn_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
@@ -611,6 +612,21 @@ def peaks(w, steps, warmup, flush):
             fn = _c_call(lib.sink_attn_peak_coissue, (e, split, ci, cb, ctypes.c_void_p(outc.data_ptr()), st))
             sc, _ = time_calls([fn], steps, warmup, flush)
             co[key][str(e)] = round(cb * 4 * ci * 8 * 32768 / (sc["median"] * 1e-3) / 1e12, 1)
+    # vector issue rate of the softmax's two main instructions, 1, 2 or 4 wavefronts per SIMD
+    lib.sink_attn_peak_valu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    vi = 8192
+    outv = torch.empty(cus * 1024, dtype=torch.float32, device="cuda")  # a float per lane, up to 1024 lanes a workgroup
+    valu = {}
+    for op, oname in ((0, "v_exp_f32"), (1, "v_fma_f32")):
+        for wps in (1, 2, 4):
+            fn = _c_call(lib.sink_attn_peak_valu, (op, wps, vi, cus, ctypes.c_void_p(outv.data_ptr()), st))
+            time_calls([fn], steps, warmup, flush)
+            torch.cuda.synchronize()
+            # lane 0 of every wavefront: shader-clock cycles of its loop; wps wavefronts share
+            # a SIMD, so the SIMD issued wps * vi * 8 instructions in that time
+            cyc = outv[: cus * 256 * wps].view(cus, 4 * wps, 64)[:, :, 0].double()
+            valu.setdefault(oname, {})[str(wps)] = round(float(cyc.median()) / (wps * vi * 8), 2)
     return {"hbm_flat_read": {"GB/s": round(hbm, 1), "frac_of_spec": round(hbm / HBM_PEAK_GBS, 4),
                               "bytes": 2 * kb, "ms": _r(s["median"]),
                               "what": f"non-temporal 16-byte loads over {w.name}'s K and V, "
@@ -623,6 +639,10 @@ def peaks(w, steps, warmup, flush):
                                                      "per SIMD; key = exp2+FMA pairs per MFMA, "
                                                      "issued after each MFMA by the same "
                                                      "wavefront or by the SIMD's second one"),
+            "valu_cycles_per_wave64_instr": dict(valu, what=f"{cus} workgroups, key = wavefronts "
+                                                            "per SIMD, each issuing 8 independent "
+                                                            "chains; shader-clock cycles per "
+                                                            "instruction issued by the SIMD"),
             "compute_units": cus}
 
 

@@ -1,7 +1,8 @@
 // Achievable-peak probes for the measurement harness (not part of the attention path):
 // how fast this chip streams HBM with the read pattern the decode kernels use, how many
-// bf16 MFMA flops it sustains when nothing else runs, and how many when softmax-like
-// vector work shares the SIMD (issued by the same wavefront or by its neighbour).  The attention kernels'
+// bf16 MFMA flops it sustains when nothing else runs, how many when softmax-like vector
+// work shares the SIMD (issued by the same wavefront or by its neighbour), and the issue
+// rate of the softmax's vector instructions.  The attention kernels'
 // roofline fractions are quoted against the spec-sheet peaks; these give the measured
 // ceilings beside them.
 #include <hip/hip_runtime.h>
@@ -124,6 +125,41 @@ __global__ __launch_bounds__(512) void coissue_kernel(int iters, float* out) {
   out[(int64_t)blockIdx.x * 512 + threadIdx.x] = s;
 }
 
+// Vector issue rate: each wavefront runs iters x 8 independent chains of one instruction
+// (OP 0: v_exp_f32 of the negated value, OP 1: v_fma_f32), W wavefronts per SIMD, no
+// memory traffic inside the loop.  out has grid * 256 * W floats: lane 0 of each
+// wavefront stores the shader-clock cycles its loop took (so the rate does not depend on
+// the clock the GPU runs at), the other lanes their sums.
+template <int OP, int W>
+__global__ __launch_bounds__(256 * W) void valu_rate_kernel(int iters, float a, float b, float* out) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.25f + 0.01f * (float)(threadIdx.x & 7) + 0.001f * (float)i;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (OP == 0) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      else x[i] = __builtin_fmaf(x[i], a, b);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  out[(int64_t)blockIdx.x * 256 * W + threadIdx.x] = (threadIdx.x & 63) == 0 ? (float)(t1 - t0) : s;
+}
+
+template <int OP>
+void launch_valu(int waves, int iters, int blocks, float* out, hipStream_t st) {
+  const dim3 g((unsigned)blocks);
+  switch (waves) {
+    case 1: hipLaunchKernelGGL((valu_rate_kernel<OP, 1>), g, dim3(256), 0, st, iters, 0.999f, 0.001f, out); break;
+    case 2: hipLaunchKernelGGL((valu_rate_kernel<OP, 2>), g, dim3(512), 0, st, iters, 0.999f, 0.001f, out); break;
+    default: hipLaunchKernelGGL((valu_rate_kernel<OP, 4>), g, dim3(1024), 0, st, iters, 0.999f, 0.001f, out); break;
+  }
+}
+
 template <int E>
 void launch_coissue(bool split, int iters, int blocks, float* out, hipStream_t st) {
   if (split)
@@ -165,6 +201,17 @@ int sink_attn_peak_coissue(int32_t pairs_per_mfma, int32_t split, int32_t iters,
     case 3: launch_coissue<3>(split != 0, iters, num_blocks, out, st); break;
     default: launch_coissue<4>(split != 0, iters, num_blocks, out, st); break;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int sink_attn_peak_valu(int32_t op, int32_t waves_per_simd, int32_t iters, int32_t num_blocks,
+                        float* out, void* stream) {
+  if (!out || iters < 1 || num_blocks < 1 || (op != 0 && op != 1) ||
+      (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4))
+    return 1;
+  const hipStream_t st = (hipStream_t)stream;
+  if (op == 0) launch_valu<0>(waves_per_simd, iters, num_blocks, out, st);
+  else launch_valu<1>(waves_per_simd, iters, num_blocks, out, st);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -37,6 +37,15 @@ int sink_attn_peak_mfma_bf16(int32_t iters, int32_t num_blocks, float* out, void
 int sink_attn_peak_coissue(int32_t pairs_per_mfma, int32_t split, int32_t iters,
                            int32_t num_blocks, float* out, void* stream);
 
+/* Vector issue rate: num_blocks workgroups of 4 * waves_per_simd wavefronts (waves_per_simd
+ * in {1, 2, 4}; one workgroup per CU fills every SIMD with that many), each wavefront
+ * issuing iters x 8 independent instructions of one kind, op 0: v_exp_f32, op 1:
+ * v_fma_f32 (num_blocks * 4 * waves_per_simd * iters * 8 wave64 instructions).
+ * out: num_blocks * 256 * waves_per_simd floats of device memory; element 64 w of a
+ * workgroup's 256 * waves_per_simd holds the shader-clock cycles wavefront w's loop took. */
+int sink_attn_peak_valu(int32_t op, int32_t waves_per_simd, int32_t iters, int32_t num_blocks,
+                        float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

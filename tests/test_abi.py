@@ -444,3 +444,37 @@ def test_decode_noalloc_validation(lib):
     assert call(q=None) == INVALID and call(out=None) == INVALID and call(ind=None) == INVALID
     assert call(ql=5) == UNSUPPORTED and call(hq=63) == INVALID and call(ns=65) == INVALID
     assert b"SCRATCH_LIMIT" in lib.sink_attn_status_str(6)
+
+
+PEAK_HEADER = os.path.join(ROOT, "include", "sink_attn_peak.h")
+
+
+def test_peak_library_exports_and_validates(lib):
+    """The achievable-peak probes (libsinkattn_peak.so) export what include/sink_attn_peak.h
+    declares and reject invalid arguments before any launch."""
+    from gqa_attention_sink_amd import build as bld
+    names = sorted(set(re.findall(r"^\s*int\s+(sink_attn_peak_[a-z_0-9]+)\(",
+                                  open(PEAK_HEADER).read(), flags=re.M)))
+    assert names == ["sink_attn_peak_coissue", "sink_attn_peak_mfma_bf16",
+                     "sink_attn_peak_stream_read", "sink_attn_peak_valu"]
+    out = subprocess.run(["nm", "-D", "--defined-only", bld.PEAK_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(ln.split()[-1] for ln in out.splitlines() if ln.strip())
+    assert not [n for n in names if n not in exported]
+    p = ctypes.CDLL(bld.PEAK_LIB)
+    i32, vp = ctypes.c_int32, ctypes.c_void_p
+    p.sink_attn_peak_valu.argtypes = [i32, i32, i32, i32, vp, vp]
+    p.sink_attn_peak_stream_read.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+    p.sink_attn_peak_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    p.sink_attn_peak_coissue.argtypes = [i32, i32, i32, i32, vp, vp]
+    for args in ((2, 1, 8, 1, FAKE), (0, 3, 8, 1, FAKE), (1, 1, 8, 1, None), (0, 4, 0, 1, FAKE),
+                 (0, 1, 8, 0, FAKE)):
+        assert p.sink_attn_peak_valu(*args, None) == 1, args
+    assert p.sink_attn_peak_stream_read(FAKE, 0, 4, FAKE, None) == 1
+    assert p.sink_attn_peak_stream_read(FAKE, 24, 4, FAKE, None) == 1      # not 16-byte sized
+    assert p.sink_attn_peak_stream_read(ctypes.c_void_p(0x1008), 32, 4, FAKE, None) == 1
+    assert p.sink_attn_peak_stream_read(FAKE, 32, 0, FAKE, None) == 1
+    assert p.sink_attn_peak_mfma_bf16(0, 4, FAKE, None) == 1
+    assert p.sink_attn_peak_mfma_bf16(8, 4, None, None) == 1
+    assert p.sink_attn_peak_coissue(5, 0, 8, 4, FAKE, None) == 1
+    assert p.sink_attn_peak_coissue(-1, 1, 8, 4, FAKE, None) == 1
